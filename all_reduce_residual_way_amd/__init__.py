@@ -1,1 +1,222 @@
-"""MI355X-native fused all-reduce + residual-add + RMSNorm epilogue (one GPU's share)."""
+"""MI355X-native fused all-reduce + residual-add + RMSNorm epilogue (one GPU's share).
+
+A thin ctypes binding over ``libfused_ar.so`` (built from ``csrc/`` by ``build.py``), with the
+same entry points as the C ABI in ``include/fused_ar.h``. This module only marshals arguments:
+every step of the operation runs in the library's HIP kernels. PyTorch supplies device memory and
+streams. If the library is not built, every call raises; there is no fallback.
+
+    from all_reduce_residual_way_amd import fused_ar_rmsnorm
+    residual_out, out = fused_ar_rmsnorm(inputs, residual, weight, eps=1e-6)
+"""
+import ctypes
+import os
+
+__all__ = [
+    "FusedArError", "library", "fused_ar_rmsnorm", "fused_ar_reduce", "fused_ar_rmsnorm_ptrs",
+    "fused_ar_reduce_ptrs", "fused_ar_rmsnorm_check_ptrs", "auto_path", "describe_launch", "strerror",
+    "OK", "ERR_INVALID", "ERR_SHAPE", "ERR_ALIGN", "ERR_ALIAS",
+    "PATH_AUTO", "PATH_ONESTAGE", "PATH_TWOSTAGE", "MAX_INPUTS", "MAX_HIDDEN",
+]
+
+LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfused_ar.so")
+
+# Values of include/fused_ar.h.
+OK, ERR_INVALID, ERR_SHAPE, ERR_ALIGN, ERR_ALIAS = 0, -1, -2, -3, -4
+PATH_AUTO, PATH_ONESTAGE, PATH_TWOSTAGE = 0, 1, 2
+MAX_INPUTS, MAX_HIDDEN = 8, 32768
+
+_VP = ctypes.c_void_p
+
+
+class _KernelLaunch(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("grid", ctypes.c_uint), ("block", ctypes.c_uint),
+                ("per_thread", ctypes.c_uint)]
+
+
+class _LaunchPlan(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int), ("kernels", ctypes.c_int), ("launch", _KernelLaunch * 2)]
+
+
+class FusedArError(RuntimeError):
+    """A non-zero status from libfused_ar.so."""
+
+    def __init__(self, status, what):
+        super().__init__(f"{what}: status {status}: {strerror(status)}")
+        self.status = status
+
+
+_lib = None
+
+
+def library():
+    """The loaded ``libfused_ar.so`` (ctypes.CDLL); raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY_PATH):
+            raise RuntimeError(
+                f"{LIBRARY_PATH} is not built; build it with "
+                "`python -c 'import __graft_entry__ as g; g.build()'` or "
+                "`python all_reduce_residual_way_amd/build.py`")
+        lib = ctypes.CDLL(LIBRARY_PATH)
+        lib.fused_ar_rmsnorm.argtypes = [ctypes.POINTER(_VP), ctypes.c_int, _VP, _VP, ctypes.c_float,
+                                         ctypes.c_int, ctypes.c_int, _VP, _VP, ctypes.c_int, _VP]
+        lib.fused_ar_rmsnorm.restype = ctypes.c_int
+        lib.fused_ar_rmsnorm_check.argtypes = [ctypes.POINTER(_VP), ctypes.c_int, _VP, _VP,
+                                               ctypes.c_float, ctypes.c_int, ctypes.c_int, _VP,
+                                               _VP, ctypes.c_int]
+        lib.fused_ar_rmsnorm_check.restype = ctypes.c_int
+        lib.fused_ar_reduce.argtypes = [ctypes.POINTER(_VP), ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, _VP, _VP]
+        lib.fused_ar_reduce.restype = ctypes.c_int
+        lib.fused_ar_auto_path.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        lib.fused_ar_auto_path.restype = ctypes.c_int
+        lib.fused_ar_describe_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                 ctypes.c_int, ctypes.POINTER(_LaunchPlan)]
+        lib.fused_ar_describe_launch.restype = ctypes.c_int
+        lib.fused_ar_strerror.argtypes = [ctypes.c_int]
+        lib.fused_ar_strerror.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def strerror(status):
+    return library().fused_ar_strerror(int(status)).decode()
+
+
+def auto_path(n, m, hidden):
+    """The path (1 or 2) that ``path=0`` selects; negative status for bad arguments."""
+    return library().fused_ar_auto_path(int(n), int(m), int(hidden))
+
+
+def describe_launch(n, m, hidden, path=PATH_AUTO):
+    """Kernels, grids and workgroup sizes of a call, as a dict; raises on bad arguments."""
+    plan = _LaunchPlan()
+    rc = library().fused_ar_describe_launch(int(n), int(m), int(hidden), int(path),
+                                            ctypes.byref(plan))
+    if rc != OK:
+        raise FusedArError(rc, "fused_ar_describe_launch")
+    return {
+        "path": plan.path,
+        "kernels": [
+            {"name": plan.launch[i].name.decode(), "grid": plan.launch[i].grid,
+             "block": plan.launch[i].block, "per_thread": plan.launch[i].per_thread}
+            for i in range(plan.kernels)
+        ],
+    }
+
+
+def _ptr_array(ptrs):
+    return (_VP * len(ptrs))(*[int(p) for p in ptrs])
+
+
+def fused_ar_rmsnorm_ptrs(input_ptrs, residual, weight, eps, m, hidden, residual_out, out,
+                          path=PATH_AUTO, stream=0):
+    """Raw call with integer device addresses and a raw stream handle; returns the status."""
+    arr = _ptr_array(input_ptrs)
+    return library().fused_ar_rmsnorm(arr, len(input_ptrs), _VP(residual), _VP(weight),
+                                      float(eps), int(m), int(hidden), _VP(residual_out), _VP(out),
+                                      int(path), _VP(stream))
+
+
+def fused_ar_rmsnorm_check_ptrs(input_ptrs, residual, weight, eps, m, hidden, residual_out, out,
+                                path=PATH_AUTO):
+    """The status fused_ar_rmsnorm would return for these arguments, without launching."""
+    arr = _ptr_array(input_ptrs)
+    return library().fused_ar_rmsnorm_check(arr, len(input_ptrs), _VP(residual), _VP(weight),
+                                            float(eps), int(m), int(hidden), _VP(residual_out),
+                                            _VP(out), int(path))
+
+
+def fused_ar_reduce_ptrs(input_ptrs, m, hidden, reduced, stream=0):
+    """Raw call of the reduce alone; returns the status."""
+    arr = _ptr_array(input_ptrs)
+    return library().fused_ar_reduce(arr, len(input_ptrs), int(m), int(hidden), _VP(reduced),
+                                     _VP(stream))
+
+
+def _check_tensor(t, name, shape, device):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.device.type != "cuda" or (device is not None and t.device != device):
+        raise ValueError(f"{name} must be on {device or 'a GPU'}, got {t.device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def fused_ar_rmsnorm(inputs, residual, weight, eps=1e-6, *, residual_out=None, out=None,
+                     path=PATH_AUTO, stream=None):
+    """The fused epilogue on one GPU.
+
+    Args:
+        inputs: list of n (1..8) bf16 CUDA tensors of shape (m, hidden), the partial sums; they
+            are reduced in fp32 in list order.
+        residual: bf16 (m, hidden). weight: bf16 (hidden,). eps: float >= 0.
+        residual_out: optional bf16 (m, hidden) output buffer; may be ``residual`` itself.
+        out: optional bf16 (m, hidden) output buffer, overlapping nothing else (the two-stage path
+            also uses it as scratch).
+        path: 0 automatic, 1 one-stage, 2 two-stage.
+        stream: torch.cuda.Stream to enqueue on (default: the current stream).
+    Returns:
+        (residual_out, out). Missing outputs are allocated with ``torch.empty_like(residual)``
+        and belong to the caller. The work is asynchronous on the stream.
+    Raises:
+        TypeError/ValueError for tensors of the wrong dtype, device, shape or layout;
+        FusedArError for a non-zero library status.
+    """
+    import torch
+    if not isinstance(inputs, (list, tuple)) or not inputs:
+        raise ValueError("inputs must be a non-empty list of tensors")
+    if not isinstance(residual, torch.Tensor) or residual.dim() != 2:
+        raise ValueError("residual must be a 2-D tensor (m, hidden)")
+    m, hidden = residual.shape
+    device = residual.device
+    for i, x in enumerate(inputs):
+        _check_tensor(x, f"inputs[{i}]", (m, hidden), device)
+    _check_tensor(residual, "residual", (m, hidden), device)
+    _check_tensor(weight, "weight", (hidden,), device)
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    if out is None:
+        out = torch.empty_like(residual)
+    _check_tensor(residual_out, "residual_out", (m, hidden), device)
+    _check_tensor(out, "out", (m, hidden), device)
+    rc = fused_ar_rmsnorm_ptrs([x.data_ptr() for x in inputs], residual.data_ptr(),
+                               weight.data_ptr(), eps, m, hidden, residual_out.data_ptr(),
+                               out.data_ptr(), path, _stream_handle(stream, device))
+    if rc != OK:
+        raise FusedArError(rc, "fused_ar_rmsnorm")
+    return residual_out, out
+
+
+def fused_ar_reduce(inputs, *, reduced=None, stream=None):
+    """The N-way reduce alone (the two-stage path's first kernel): bf16 of the fp32 sum of
+    ``inputs`` (list of bf16 (m, hidden) CUDA tensors) in list order. Returns ``reduced``."""
+    import torch
+    if not isinstance(inputs, (list, tuple)) or not inputs:
+        raise ValueError("inputs must be a non-empty list of tensors")
+    x0 = inputs[0]
+    if not isinstance(x0, torch.Tensor) or x0.dim() != 2:
+        raise ValueError("inputs must be 2-D tensors (m, hidden)")
+    m, hidden = x0.shape
+    for i, x in enumerate(inputs):
+        _check_tensor(x, f"inputs[{i}]", (m, hidden), x0.device)
+    if reduced is None:
+        reduced = torch.empty_like(x0)
+    _check_tensor(reduced, "reduced", (m, hidden), x0.device)
+    rc = fused_ar_reduce_ptrs([x.data_ptr() for x in inputs], m, hidden, reduced.data_ptr(),
+                              _stream_handle(stream, x0.device))
+    if rc != OK:
+        raise FusedArError(rc, "fused_ar_reduce")
+    return reduced

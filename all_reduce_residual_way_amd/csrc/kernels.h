@@ -1,0 +1,163 @@
+// kernels.h - the gfx950 kernels of the fused all-reduce + residual + RMSNorm epilogue.
+//
+//   k_rows<N, PPT>     one workgroup per row: N-way reduce, residual add, square-sum, RMSNorm.
+//                      With N inputs it is the one-stage path (aiter PR #3817, Technical Details >
+//                      1stage); with N = 1 reading the reduced rows it is stage 2 of the two-stage
+//                      path (Technical Details > 2stage > stage-2 RMSNorm reduce).
+//   k_flat_reduce<N>   stage 1 of the two-stage path: one thread per pack, N-way fp32 reduce,
+//                      one bf16 store, no LDS and no workgroup barrier (Technical Details >
+//                      2stage > reduce-scatter).
+//
+// Both read and write 16-byte packs of eight bf16; a row of `hidden` elements is hidden / 8 packs
+// and consecutive lanes touch consecutive packs, so every wave access is 1 KiB contiguous.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "bf16x8.h"
+#include "wave_sum.h"
+
+namespace fa {
+
+constexpr int kMaxInputs = 8;
+constexpr int kMaxWaves = 16;  // 1024 threads
+
+struct RowArgs {
+    const u32x4 *in[kMaxInputs];  // N partial sums, [m, packs] packs each
+    const u32x4 *residual;        // [m, packs]
+    const u32x4 *weight;          // [packs]
+    u32x4 *residual_out;          // [m, packs]; may equal residual
+    u32x4 *out;                   // [m, packs]; may equal in[0] when N == 1 (stage 2)
+    float eps;
+    float hidden;                 // row length as a float, the divisor of the mean
+    int packs;                    // packs per row = hidden / 8
+    int rows;                     // m
+};
+
+struct FlatArgs {
+    const u32x4 *in[kMaxInputs];
+    u32x4 *out;
+    size_t total_packs;
+};
+
+// Sum of the N packs in input order, in fp32, starting from input 0.
+template <int N>
+__device__ __forceinline__ F8 reduce_packs(const u32x4 (&x)[N])
+{
+    F8 acc = widen(x[0]);
+#pragma unroll
+    for (int i = 1; i < N; ++i)
+        add_into(acc, widen(x[i]));
+    return acc;
+}
+
+// A pack at a byte offset from a wave-uniform base: the base stays in scalar registers and the
+// per-lane offset is 32 bits, which lets the loads and stores use scalar-base addressing instead
+// of a 64-bit address per lane per buffer.
+__device__ __forceinline__ u32x4 load_pack(const char *base, uint32_t off)
+{
+    return *reinterpret_cast<const u32x4 *>(base + off);
+}
+
+__device__ __forceinline__ void store_pack(char *base, uint32_t off, u32x4 v)
+{
+    *reinterpret_cast<u32x4 *>(base + off) = v;
+}
+
+// One workgroup handles rows blockIdx.x, blockIdx.x + gridDim.x, ...; thread t handles packs
+// t, t + blockDim.x, ..., PPT of them, of each row. For each of its packs a thread loads the N
+// inputs and the residual, reduces, writes residual_out and accumulates the square-sum, keeping
+// only the bf16 residual_out pack; one workgroup reduction then gives the row statistic and the
+// normalised row is written from those registers.
+template <int N, int PPT>
+__global__ void __launch_bounds__(1024) k_rows(RowArgs a)
+{
+    __shared__ float slots[2][kMaxWaves];  // alternate per row, so one barrier per row suffices
+    const uint32_t tid = threadIdx.x;
+    const uint32_t nthreads = blockDim.x;
+    const uint32_t packs = (uint32_t)a.packs;
+    const char *weight = reinterpret_cast<const char *>(a.weight);
+    int parity = 0;
+
+    for (int row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        const size_t row_bytes = (size_t)row * packs * sizeof(u32x4);
+        const char *in[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            in[i] = reinterpret_cast<const char *>(a.in[i]) + row_bytes;
+        const char *residual = reinterpret_cast<const char *>(a.residual) + row_bytes;
+        char *residual_out = reinterpret_cast<char *>(a.residual_out) + row_bytes;
+        char *out = reinterpret_cast<char *>(a.out) + row_bytes;
+
+        u32x4 ro[PPT];
+        u32x4 w[PPT];
+        float ss = 0.0f;
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
+            const uint32_t p = tid + k * nthreads;
+            if (p < packs) {
+                const uint32_t off = p * (uint32_t)sizeof(u32x4);
+                u32x4 x[N];
+#pragma unroll
+                for (int i = 0; i < N; ++i)
+                    x[i] = load_pack(in[i], off);
+                const u32x4 res = load_pack(residual, off);
+                w[k] = load_pack(weight, off);
+                // all of this slot's loads are in flight before any arithmetic waits on one
+                __builtin_amdgcn_sched_barrier(0);
+                F8 sum = widen(narrow(reduce_packs<N>(x)));  // the reduced value, in bf16
+                add_into(sum, widen(res));
+                ro[k] = narrow(sum);
+                store_pack(residual_out, off, ro[k]);
+                const F8 y = widen(ro[k]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    ss = __builtin_fmaf(y.v[e], y.v[e], ss);  // y * y is exact in fp32
+            }
+        }
+
+        const float total = block_sum(ss, slots[parity]);
+        parity ^= 1;
+        const float rstd = 1.0f / __builtin_sqrtf(total / a.hidden + a.eps);
+
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
+            const uint32_t p = tid + k * nthreads;
+            if (p < packs) {
+                const uint32_t off = p * (uint32_t)sizeof(u32x4);
+                const F8 y = widen(ro[k]);
+                const F8 g = widen(w[k]);
+                F8 o;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    o.v[e] = (y.v[e] * rstd) * g.v[e];
+                store_pack(out, off, narrow(o));
+            }
+        }
+    }
+}
+
+// Flat N-way reduce: workgroup b handles the blockDim.x packs starting at pack b * blockDim.x,
+// then strides by the whole grid (one pass when the grid covers the problem, which it does up to
+// 2^30 packs).
+template <int N>
+__global__ void __launch_bounds__(1024) k_flat_reduce(FlatArgs a)
+{
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    const uint32_t off = threadIdx.x * (uint32_t)sizeof(u32x4);
+    for (size_t first = (size_t)blockIdx.x * blockDim.x; first < a.total_packs; first += stride) {
+        if (first + threadIdx.x >= a.total_packs)
+            break;
+        const size_t bytes = first * sizeof(u32x4);
+        u32x4 x[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            x[i] = load_pack(reinterpret_cast<const char *>(a.in[i]) + bytes, off);
+        __builtin_amdgcn_sched_barrier(0);  // all N loads in flight before the first add
+        store_pack(reinterpret_cast<char *>(a.out) + bytes, off, narrow(reduce_packs<N>(x)));
+    }
+}
+
+}  // namespace fa

@@ -1,0 +1,63 @@
+// wave_sum.h - sum of one float per lane over a 64-lane wavefront with DPP, and over a workgroup
+// with one LDS exchange. The RMSNorm square-sum reduction of both paths (aiter PR #3817,
+// Technical Details > 1stage and > 2stage > stage-2 RMSNorm reduce: a DPP tree inside the wave).
+//
+// Every step below adds a lane's value to a partner lane's value with the two lanes using each
+// other as partners, so both compute the same sum (IEEE addition commutes) and every lane of a
+// group ends with bit-identical partial sums. The tree is fixed, so the result is the same on
+// every run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace fa {
+
+// DPP lane-select controls (CDNA "data parallel primitives" encodings).
+enum : int {
+    kDppQuadXor1 = 0xB1,     // quad_perm [1,0,3,2]: lane i reads lane i ^ 1
+    kDppQuadXor2 = 0x4E,     // quad_perm [2,3,0,1]: lane i reads lane i ^ 2
+    kDppRowHalfMirror = 0x141, // lane i reads lane 7 - i within each group of 8
+    kDppRowMirror = 0x140,   // lane i reads lane 15 - i within each row of 16
+};
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_partner(float x)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float lane_value(float x, int lane)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+
+// Sum over the 64 lanes; the result is uniform across the wave.
+__device__ __forceinline__ float wave_sum(float x)
+{
+    x = x + dpp_partner<kDppQuadXor1>(x);      // pairs
+    x = x + dpp_partner<kDppQuadXor2>(x);      // quads
+    x = x + dpp_partner<kDppRowHalfMirror>(x); // the two quads of each group of 8
+    x = x + dpp_partner<kDppRowMirror>(x);     // the two halves of each 16-lane row
+    // every lane of a row now holds that row's sum; combine the four rows
+    return (lane_value(x, 0) + lane_value(x, 16)) + (lane_value(x, 32) + lane_value(x, 48));
+}
+
+// Sum over the workgroup (blockDim.x a multiple of 64, at most 1024): wave sums, one barrier,
+// then every thread adds the per-wave sums in wave order. `slots` is LDS with room for one float
+// per wave; all threads of the workgroup must call this.
+__device__ __forceinline__ float block_sum(float x, float *slots)
+{
+    const float w = wave_sum(x);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0)
+        slots[wave] = w;
+    __syncthreads();
+    const int waves = blockDim.x >> 6;
+    float total = slots[0];
+    for (int i = 1; i < waves; ++i)
+        total = total + slots[i];
+    return total;
+}
+
+}  // namespace fa

@@ -1,0 +1,154 @@
+/*
+ * fused_ar.h - C ABI of libfused_ar.so: the fused all-reduce + residual-add + RMSNorm epilogue
+ * on one MI355X (gfx950), for the N partial sums that N tensor-parallel ranks would hold.
+ *
+ * What it computes (one GPU's share of the fused operator):
+ *   reduced[r][j]      = bf16( fp32 sum of inputs[0][r][j], ..., inputs[n-1][r][j], left to right )
+ *   residual_out[r][j] = bf16( reduced[r][j] + residual[r][j] )
+ *   out[r][j]          = bf16( residual_out[r][j] / sqrt(mean_j(residual_out[r][j]^2) + eps) * weight[j] )
+ * - the reduce: "perf: optimize fused AllReduce + RMSNorm (custom_all_reduce)" (ROCm/aiter
+ *   PR #3817), Technical Details > 2stage > reduce-scatter (per-pack fp32 reduce across the ranks
+ *   in the order ptrs[0..ngpus-1], then a downcast to bf16);
+ * - residual add and RMSNorm: the fused operator of "perf(comm): add opt-in Triton AR+RMSNorm
+ *   backend" (lightseekorg/tokenspeed PR #968), Summary (AI), on contiguous bf16 (tokens, hidden)
+ *   tensors with a bf16 weight; the RMSNorm square-sum is a per-row reduction (aiter PR #3817,
+ *   Technical Details > 1stage and > 2stage > stage-2 RMSNorm reduce).
+ * Conversions to bf16 round to nearest, ties to even. The sums of the reduce are exact binary32
+ * additions in the fixed order, so `reduced` and `residual_out` are reproducible bit for bit; the
+ * RMSNorm statistic is an fp32 sum in a fixed tree, so `out` is deterministic run to run.
+ *
+ * Conventions for every entry point:
+ * - bf16 values are raw 16-bit patterns (fa_bf16). Every [m, hidden] array is row-major and
+ *   contiguous, so row r starts hidden elements after row r-1; `weight` has hidden elements.
+ * - Pointers named "device" are device (HBM) addresses on the current HIP device; the caller owns
+ *   all of them. The library allocates nothing, keeps no state between calls and never
+ *   synchronises: it enqueues kernels on `stream` and returns. Buffers must stay valid until the
+ *   stream has executed the work. Calls may be captured into a HIP graph (the pointers are copied
+ *   into the kernel arguments and are baked into the graph).
+ * - `inputs` is a HOST array of n device pointers; it is read during the call only.
+ * - Every argument check happens before any HIP call. A rejected call launches nothing.
+ * - Return value: FUSED_AR_OK (0), one of the negative FUSED_AR_ERR_* codes below, or a positive
+ *   hipError_t reported by the kernel launch. fused_ar_strerror() names each.
+ */
+#ifndef FUSED_AR_H
+#define FUSED_AR_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t fa_bf16; /* raw bfloat16 bit pattern */
+
+enum {
+    FUSED_AR_OK = 0,
+    FUSED_AR_ERR_INVALID = -1, /* null pointer, n outside [1, 8], m < 0, hidden <= 0, eps < 0 or
+                                  not finite, path outside {0, 1, 2}, pointer range wraps */
+    FUSED_AR_ERR_SHAPE = -2,   /* hidden not a multiple of 8, or above FUSED_AR_MAX_HIDDEN */
+    FUSED_AR_ERR_ALIGN = -3,   /* a device pointer not 16-byte aligned */
+    FUSED_AR_ERR_ALIAS = -4    /* a forbidden overlap of buffers (see fused_ar_rmsnorm) */
+};
+
+#define FUSED_AR_MAX_INPUTS 8
+#define FUSED_AR_MAX_HIDDEN 32768
+
+/* Path selector values. */
+enum {
+    FUSED_AR_PATH_AUTO = 0,     /* fused_ar_auto_path(n, m, hidden) */
+    FUSED_AR_PATH_ONESTAGE = 1, /* one kernel, one row per workgroup */
+    FUSED_AR_PATH_TWOSTAGE = 2  /* flat reduce kernel, then residual + RMSNorm kernel */
+};
+
+/*
+ * fused_ar_rmsnorm - the whole epilogue: reduce, residual add, RMSNorm.
+ *
+ *   inputs        host array of n device pointers, each [m, hidden] bf16; the reduce order is the
+ *                 array order (aiter PR #3817, Technical Details > 2stage > reduce-scatter).
+ *   n             number of partial sums, 1..FUSED_AR_MAX_INPUTS.
+ *   residual      device [m, hidden] bf16.
+ *   weight        device [hidden] bf16.
+ *   eps           >= 0 and finite; added to the mean of squares inside the square root. With
+ *                 eps == 0 a row that is all zero gives NaN (0 * inf), as the formula does.
+ *   m, hidden     rows (tokens) and row length; m == 0 returns FUSED_AR_OK and launches nothing
+ *                 (no pointer is looked at); hidden % 8 == 0 and hidden <= FUSED_AR_MAX_HIDDEN.
+ *   residual_out  device [m, hidden] bf16, written. May be exactly `residual` (in place); it must
+ *                 not otherwise overlap `residual`, and must not overlap an input or the weight.
+ *   out           device [m, hidden] bf16, written. Must not overlap any other buffer. The
+ *                 two-stage path also uses it as its scratch: stage 1 writes the reduced rows
+ *                 there and stage 2 overwrites them with the normalised rows.
+ *   path          FUSED_AR_PATH_AUTO, _ONESTAGE or _TWOSTAGE (aiter PR #3817, Technical Details >
+ *                 1stage / 2stage); both give bit-identical residual_out.
+ *   stream        HIP stream the kernels are enqueued on (0 = the null stream).
+ * Inputs may overlap one another and the weight may overlap inputs or the residual (all are only
+ * read). All device pointers must be 16-byte aligned.
+ */
+int fused_ar_rmsnorm(const fa_bf16 *const *inputs, int n, const fa_bf16 *residual,
+                     const fa_bf16 *weight, float eps, int m, int hidden, fa_bf16 *residual_out,
+                     fa_bf16 *out, int path, hipStream_t stream);
+
+/*
+ * fused_ar_rmsnorm_check - the argument checks of fused_ar_rmsnorm alone, with the same arguments
+ * (no stream): returns the status fused_ar_rmsnorm would return before launching anything
+ * (FUSED_AR_OK if it would launch). Makes no HIP call. A preflight for callers that must decide
+ * on a fallback before work is enqueued (the concern behind the decline/fallback review threads
+ * of tokenspeed PR #968).
+ */
+int fused_ar_rmsnorm_check(const fa_bf16 *const *inputs, int n, const fa_bf16 *residual,
+                           const fa_bf16 *weight, float eps, int m, int hidden,
+                           const fa_bf16 *residual_out, const fa_bf16 *out, int path);
+
+/*
+ * fused_ar_reduce - the reduce alone, the two-stage path's first kernel ("a flat reduce-scatter":
+ * aiter PR #3817, Technical Details > 2stage > reduce-scatter): one thread per 8-element pack,
+ * fp32 sum over the n inputs in array order, one bf16 store; no LDS, no workgroup barrier.
+ *
+ *   inputs   host array of n device pointers, each m * hidden bf16 (contiguous).
+ *   n        1..FUSED_AR_MAX_INPUTS.
+ *   m, hidden  m >= 0 (0 launches nothing); hidden > 0 and a multiple of 8 (no upper bound).
+ *   reduced  device m * hidden bf16, written; must not overlap any input.
+ *   stream   HIP stream.
+ * Errors as for fused_ar_rmsnorm. All pointers 16-byte aligned.
+ */
+int fused_ar_reduce(const fa_bf16 *const *inputs, int n, int m, int hidden, fa_bf16 *reduced,
+                    hipStream_t stream);
+
+/*
+ * fused_ar_auto_path - the path FUSED_AR_PATH_AUTO takes: one-stage for m <= 32 when n <= 4 and
+ * for m <= 16 when n > 4, two-stage above (the selection thresholds that aiter PR #3817, Test
+ * Results, quotes for TP4 and TP8, extended to other n by n <= 4 / n > 4).
+ * Returns 1 or 2, or FUSED_AR_ERR_INVALID for n outside [1, 8] or m < 0. `hidden` is not used
+ * by the current rule.
+ */
+int fused_ar_auto_path(int n, int m, int hidden);
+
+/* One kernel launch of a call, as fused_ar_describe_launch reports it. */
+typedef struct {
+    char name[32];        /* kernel name: "onestage", "stage1_reduce" or "stage2_norm" */
+    unsigned grid;        /* workgroups */
+    unsigned block;       /* threads per workgroup (a multiple of 64) */
+    unsigned per_thread;  /* 8-element packs each thread handles per row (or per stride) */
+} fused_ar_kernel_launch;
+
+typedef struct {
+    int path;                       /* resolved path: 1 or 2 */
+    int kernels;                    /* launches per call: 1 or 2 */
+    fused_ar_kernel_launch launch[2];
+} fused_ar_launch_plan;
+
+/*
+ * fused_ar_describe_launch - the kernels, grids and workgroup sizes fused_ar_rmsnorm would use
+ * for (n, m, hidden, path), without launching anything. For benchmarks and tests.
+ * Returns FUSED_AR_OK, or the error fused_ar_rmsnorm would give for these scalars.
+ */
+int fused_ar_describe_launch(int n, int m, int hidden, int path, fused_ar_launch_plan *plan);
+
+/* fused_ar_strerror - a static, human-readable description of a status code. Never NULL. */
+const char *fused_ar_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FUSED_AR_H */

@@ -1,0 +1,188 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every function include/fused_ar.h
+declares, and rejects bad arguments with the documented codes before any HIP call (so none of
+these tests needs a GPU; no test here launches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import all_reduce_residual_way_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fused_ar.h")
+
+# Fake, 16-byte-aligned, non-overlapping "device addresses". Validation only compares them.
+MB = 1 << 20
+
+
+def addr(i):
+    return 0x7F0000000000 + i * 1024 * MB
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fused_ar_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert {"fused_ar_rmsnorm", "fused_ar_reduce", "fused_ar_auto_path",
+            "fused_ar_describe_launch", "fused_ar_strerror"} <= set(names)
+
+
+def test_library_exports_every_declared_function():
+    lib = ctypes.CDLL(fa.LIBRARY_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in fused_ar.h but not exported"
+
+
+def test_header_constants_match_binding():
+    with open(HEADER) as f:
+        text = f.read()
+    for name, value in [("FUSED_AR_OK", fa.OK), ("FUSED_AR_ERR_INVALID", fa.ERR_INVALID),
+                        ("FUSED_AR_ERR_SHAPE", fa.ERR_SHAPE), ("FUSED_AR_ERR_ALIGN", fa.ERR_ALIGN),
+                        ("FUSED_AR_ERR_ALIAS", fa.ERR_ALIAS), ("FUSED_AR_PATH_AUTO", fa.PATH_AUTO),
+                        ("FUSED_AR_PATH_ONESTAGE", fa.PATH_ONESTAGE),
+                        ("FUSED_AR_PATH_TWOSTAGE", fa.PATH_TWOSTAGE)]:
+        assert re.search(rf"\b{name}\s*=\s*{value}\b", text), name
+    assert re.search(rf"#define FUSED_AR_MAX_INPUTS {fa.MAX_INPUTS}\b", text)
+    assert re.search(rf"#define FUSED_AR_MAX_HIDDEN {fa.MAX_HIDDEN}\b", text)
+
+
+def call(n=4, m=8, hidden=4096, eps=1e-6, path=1, inputs=None, residual=None, weight=None,
+         residual_out=None, out=None, check_only=False):
+    ins = inputs if inputs is not None else [addr(i) for i in range(n)]
+    args = (ins, addr(10) if residual is None else residual, addr(11) if weight is None else weight,
+            eps, m, hidden, addr(12) if residual_out is None else residual_out,
+            addr(13) if out is None else out, path)
+    if check_only:
+        return fa.fused_ar_rmsnorm_check_ptrs(*args)
+    return fa.fused_ar_rmsnorm_ptrs(*args, 0)
+
+
+BAD_CALLS = [
+    (dict(n=0), fa.ERR_INVALID),
+    (dict(n=9), fa.ERR_INVALID),
+    (dict(m=-1), fa.ERR_INVALID),
+    (dict(hidden=0), fa.ERR_INVALID),
+    (dict(hidden=-8), fa.ERR_INVALID),
+    (dict(eps=-1e-6), fa.ERR_INVALID),
+    (dict(eps=float("nan")), fa.ERR_INVALID),
+    (dict(eps=float("inf")), fa.ERR_INVALID),
+    (dict(path=3), fa.ERR_INVALID),
+    (dict(path=-1), fa.ERR_INVALID),
+    (dict(residual=0), fa.ERR_INVALID),
+    (dict(weight=0), fa.ERR_INVALID),
+    (dict(residual_out=0), fa.ERR_INVALID),
+    (dict(out=0), fa.ERR_INVALID),
+    (dict(inputs=[addr(0), 0, addr(2)]), fa.ERR_INVALID),
+    (dict(hidden=4100), fa.ERR_SHAPE),
+    (dict(hidden=32776), fa.ERR_SHAPE),
+    (dict(inputs=[addr(0) + 8]), fa.ERR_ALIGN),
+    (dict(residual=addr(10) + 2), fa.ERR_ALIGN),
+    (dict(weight=addr(11) + 4), fa.ERR_ALIGN),
+    (dict(residual_out=addr(12) + 8), fa.ERR_ALIGN),
+    (dict(out=addr(13) + 1), fa.ERR_ALIGN),
+    (dict(out=addr(1)), fa.ERR_ALIAS),                       # out == an input
+    (dict(out=addr(10) + 4096), fa.ERR_ALIAS),               # out overlaps residual
+    (dict(out=addr(11)), fa.ERR_ALIAS),                      # out overlaps weight
+    (dict(out=addr(12)), fa.ERR_ALIAS),                      # out == residual_out
+    (dict(residual_out=addr(2)), fa.ERR_ALIAS),              # residual_out == an input
+    (dict(residual_out=addr(11) - 16), fa.ERR_ALIAS),        # residual_out overlaps weight
+    (dict(residual_out=addr(10) + 16), fa.ERR_ALIAS),        # partial overlap with residual
+    (dict(inputs=[0xFFFFFFFFFFFF0000]), fa.ERR_INVALID),     # range wraps the address space
+]
+
+
+@pytest.mark.parametrize("kwargs,code", BAD_CALLS)
+def test_rejected_before_launch(kwargs, code):
+    kwargs = dict(kwargs)
+    kwargs.setdefault("n", len(kwargs["inputs"]) if "inputs" in kwargs else 4)
+    assert call(**kwargs) == code
+    assert call(check_only=True, **kwargs) == code
+
+
+def test_valid_arguments_pass_the_check():
+    assert call(check_only=True) == fa.OK
+    for path in (0, 1, 2):
+        assert call(check_only=True, n=8, m=8192, hidden=8192, path=path) == fa.OK
+    # Allowed overlaps: inputs equal to each other, the weight inside an input (all read only),
+    # and residual_out == residual (in place).
+    assert call(check_only=True, n=3, inputs=[addr(0), addr(0), addr(1)], weight=addr(0),
+                residual_out=addr(10)) == fa.OK
+    # hidden at the maximum, eps == 0.
+    assert call(check_only=True, hidden=32768, eps=0.0) == fa.OK
+
+
+def test_m_zero_launches_nothing():
+    # m == 0 returns success before any pointer is looked at (all null here).
+    assert fa.fused_ar_rmsnorm_ptrs([0, 0], 0, 0, 1e-6, 0, 4096, 0, 0, fa.PATH_AUTO, 0) == fa.OK
+    assert fa.fused_ar_reduce_ptrs([0, 0, 0], 0, 4096, 0, 0) == fa.OK
+
+
+def test_reduce_checks():
+    ins = [addr(i) for i in range(4)]
+    assert fa.fused_ar_reduce_ptrs(ins, 8, 12, addr(20), 0) == fa.ERR_SHAPE
+    assert fa.fused_ar_reduce_ptrs(ins, -1, 16, addr(20), 0) == fa.ERR_INVALID
+    assert fa.fused_ar_reduce_ptrs([], 8, 16, addr(20), 0) == fa.ERR_INVALID
+    assert fa.fused_ar_reduce_ptrs(ins, 8, 16, 0, 0) == fa.ERR_INVALID
+    assert fa.fused_ar_reduce_ptrs(ins, 8, 16, addr(20) + 8, 0) == fa.ERR_ALIGN
+    assert fa.fused_ar_reduce_ptrs(ins, 8, 16, addr(3), 0) == fa.ERR_ALIAS
+
+
+def test_auto_path_rule():
+    # One-stage up to m = 32 for n <= 4 and up to m = 16 for n > 4.
+    for n in range(1, 9):
+        limit = 32 if n <= 4 else 16
+        assert fa.auto_path(n, 0, 4096) == fa.PATH_ONESTAGE
+        assert fa.auto_path(n, limit, 4096) == fa.PATH_ONESTAGE
+        assert fa.auto_path(n, limit + 1, 4096) == fa.PATH_TWOSTAGE
+    assert fa.auto_path(0, 1, 4096) == fa.ERR_INVALID
+    assert fa.auto_path(9, 1, 4096) == fa.ERR_INVALID
+    assert fa.auto_path(4, -1, 4096) == fa.ERR_INVALID
+
+
+@pytest.mark.parametrize("hidden", [8, 512, 520, 2880, 4096, 7168, 8192, 8200, 16384, 32768])
+def test_launch_geometry_covers_each_row(hidden):
+    packs = hidden // 8
+    for path in (1, 2):
+        plan = fa.describe_launch(8, 100, hidden, path)
+        rows = plan["kernels"][-1]
+        assert rows["name"] == ("onestage" if path == 1 else "stage2_norm")
+        assert rows["grid"] == 100
+        assert rows["block"] % 64 == 0 and 64 <= rows["block"] <= 1024
+        assert rows["block"] * rows["per_thread"] >= packs
+        assert rows["block"] * rows["per_thread"] - packs < 64 * rows["per_thread"]
+        if path == 2:
+            flat = plan["kernels"][0]
+            assert flat["name"] == "stage1_reduce" and flat["block"] == 256
+            assert flat["grid"] * flat["block"] * flat["per_thread"] >= 100 * packs
+
+
+def test_launch_geometry_auto_and_empty():
+    assert fa.describe_launch(8, 16, 7168)["path"] == 1
+    assert fa.describe_launch(8, 17, 7168)["path"] == 2
+    assert fa.describe_launch(4, 0, 7168, 1)["kernels"] == []
+    with pytest.raises(fa.FusedArError):
+        fa.describe_launch(4, 8, 12, 1)
+
+
+def test_strerror():
+    assert fa.strerror(fa.OK) == "success"
+    for code in (fa.ERR_INVALID, fa.ERR_SHAPE, fa.ERR_ALIGN, fa.ERR_ALIAS):
+        assert fa.strerror(code) and fa.strerror(code) != "unknown status"
+    assert fa.strerror(-99) == "unknown status"
+
+
+def test_binding_rejects_bad_tensors_without_a_gpu():
+    import torch
+    x = torch.zeros(4, 16, dtype=torch.bfloat16)  # CPU tensors: rejected before any call
+    with pytest.raises(ValueError):
+        fa.fused_ar_rmsnorm([x], x, torch.zeros(16, dtype=torch.bfloat16))
+    with pytest.raises(TypeError):
+        fa.fused_ar_rmsnorm([x.float()], x, torch.zeros(16, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        fa.fused_ar_rmsnorm([], x, x[0])

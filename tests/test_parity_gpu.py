@@ -1,0 +1,311 @@
+"""Parity of the HIP path with the CPU oracle, element by element, through the C ABI.
+
+Bar: `residual_out` and the reduce bit-exact; `out` within 1 bf16 ulp (the kernel's fp32 row
+statistic versus the oracle's binary64 one); no NaN. Problems the oracle finishes in seconds are
+compared whole; the full-size workloads are compared on sampled rows (rows are independent, so
+the oracle computes exactly those rows), always including the first and last row and every
+special row of the stress workload.
+"""
+import numpy as np
+import pytest
+import torch
+
+import all_reduce_residual_way_amd as fa
+import golden_cases
+import oracle
+from all_reduce_residual_way_amd import synth
+from ulp import is_nan, ulp_diff
+
+pytestmark = pytest.mark.gpu
+
+OUT_ULP = 1  # tolerance on `out`, in bf16 units in the last place
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    fa.library()  # raises if the HIP library is not built
+    yield
+
+
+def dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def host(t):
+    return t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def announce(what):
+    print(f"[gpu case] {what}", flush=True)
+
+
+def run_gpu(p, path, in_place=False):
+    ins = [dev(x) for x in p.inputs]
+    res = dev(p.residual)
+    w = dev(p.weight)
+    ro = res if in_place else torch.empty_like(res)
+    out = torch.empty_like(res)
+    fa.fused_ar_rmsnorm(ins, res, w, p.eps, residual_out=ro, out=out, path=path)
+    torch.cuda.synchronize()
+    return host(ro), host(out)
+
+
+def sample_rows(p, count=48, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = {0, p.m - 1}
+    rows |= set(rng.choice(p.m, size=min(count, p.m), replace=False).tolist())
+    rows |= set(p.meta.get("zero_rows", [])) | set(p.meta.get("big_rows", []))
+    return np.array(sorted(rows))
+
+
+def oracle_rows(p, rows=None):
+    if rows is None:
+        return oracle.fused(p.inputs, p.residual, p.weight, p.eps)
+    return oracle.fused([x[rows] for x in p.inputs], p.residual[rows], p.weight, p.eps)
+
+
+def assert_parity(name, got_ro, got_out, want_ro, want_out):
+    bad = np.argwhere(got_ro != want_ro)
+    assert bad.size == 0, (
+        f"{name}: residual_out differs at {len(bad)} elements, first {tuple(bad[0])}: "
+        f"gpu {got_ro[tuple(bad[0])]:#06x} oracle {want_ro[tuple(bad[0])]:#06x}")
+    assert not is_nan(got_out).any(), f"{name}: NaN in out"
+    d = ulp_diff(got_out, want_out)
+    assert d.max() <= OUT_ULP, (
+        f"{name}: out differs by {d.max()} ulp at {tuple(np.argwhere(d == d.max())[0])}")
+
+
+def check_problem(p, path, sampled=False):
+    name = f"{p.name} n={p.n} m={p.m} hidden={p.hidden} path={path}"
+    announce(name)
+    ro, out = run_gpu(p, path)
+    if sampled:
+        rows = sample_rows(p)
+        want_ro, want_out = oracle_rows(p, rows)
+        assert_parity(name, ro[rows], out[rows], want_ro, want_out)
+    else:
+        want_ro, want_out = oracle_rows(p)
+        assert_parity(name, ro, out, want_ro, want_out)
+    return ro, out
+
+
+# ------------------------------------------------------------------------- the workloads
+
+def workload_cases():
+    cases = []
+    for wname, w in synth.WORKLOADS.items():
+        ms = w["ms"] if w["ms"] is not None else synth.stress_m_values(0)
+        paths = sorted(set(w["paths"]) | {1, 2})  # every workload on both paths, and its own
+        for m in ms:
+            for path in paths:
+                cases.append(pytest.param(wname, m, path, id=f"{wname}-m{m}-p{path}"))
+    return cases
+
+
+@pytest.mark.parametrize("wname,m,path", workload_cases())
+def test_workload(wname, m, path):
+    w = synth.WORKLOADS[wname]
+    seed = 1000 + m
+    p = synth.make_problem(w["n"], m, w["hidden"], seed=seed, eps=w["eps"], dist=w["dist"],
+                           name=wname)
+    sampled = m * w["hidden"] * w["n"] > 8 * 1024 * 7168
+    check_problem(p, path, sampled=sampled)
+
+
+def test_paths_agree_bit_for_bit():
+    """Path 1 and path 2 give identical residual_out (the reduce order is the same) and, since
+    stage 2 is the same row kernel over the same bf16 values, identical out."""
+    for n, m, hidden in [(8, 16, 7168), (4, 100, 4096), (8, 17, 2880), (3, 7, 520)]:
+        p = synth.make_problem(n, m, hidden, seed=7)
+        announce(f"paths agree n={n} m={m} hidden={hidden}")
+        r1 = run_gpu(p, 1)
+        r2 = run_gpu(p, 2)
+        assert np.array_equal(r1[0], r2[0]) and np.array_equal(r1[1], r2[1])
+
+
+def test_auto_path_matches_explicit():
+    for n, m in [(8, 16), (8, 17), (4, 32), (4, 33)]:
+        p = synth.make_problem(n, m, 2880, seed=8)
+        announce(f"auto n={n} m={m}")
+        r0 = run_gpu(p, 0)
+        r = run_gpu(p, fa.auto_path(n, m, 2880))
+        assert np.array_equal(r0[0], r[0]) and np.array_equal(r0[1], r[1])
+
+
+# ------------------------------------------------------------------------- the reduce alone
+
+@pytest.mark.parametrize("n,m,hidden", [(1, 3, 8), (2, 5, 24), (3, 7, 520), (4, 64, 7168),
+                                        (5, 33, 2880), (6, 1, 32768), (7, 9, 1000),
+                                        (8, 257, 7168), (8, 4096, 7168)])
+def test_reduce_bit_exact(n, m, hidden):
+    p = synth.make_problem(n, m, hidden, seed=n * 100 + m)
+    announce(f"reduce n={n} m={m} hidden={hidden}")
+    red = fa.fused_ar_reduce([dev(x) for x in p.inputs])
+    torch.cuda.synchronize()
+    assert np.array_equal(host(red), oracle.reduce(p.inputs))
+
+
+def test_reduce_full_exponent_range():
+    """Random finite bf16 bits across the whole exponent range (subnormals included): the fp32
+    sums, their overflow to infinity and their subnormal results match the oracle exactly."""
+    rng = np.random.default_rng(5)
+    for n in (2, 5, 8):
+        ins = []
+        for _ in range(n):
+            b = rng.integers(0, 0x10000, (16, 512), dtype=np.uint32).astype(np.uint16)
+            b[(b & 0x7F80) == 0x7F80] &= 0xBFFF   # no Inf/NaN inputs
+            ins.append(b)
+        announce(f"reduce exponent range n={n}")
+        red = fa.fused_ar_reduce([dev(x) for x in ins])
+        torch.cuda.synchronize()
+        assert np.array_equal(host(red), oracle.reduce(ins))
+
+
+def test_reduce_subnormal_sums():
+    """Tiny inputs whose fp32 sums are subnormal: kept, not flushed to zero."""
+    rng = np.random.default_rng(6)
+    ins = [(rng.integers(0, 0x80, (4, 256)) | (rng.integers(0, 2, (4, 256)) << 15)).astype(np.uint16)
+           for _ in range(4)]  # bf16 subnormals: exponent field 0
+    announce("reduce subnormals")
+    red = fa.fused_ar_reduce([dev(x) for x in ins])
+    torch.cuda.synchronize()
+    want = oracle.reduce(ins)
+    assert np.array_equal(host(red), want)
+    assert (want & 0x7FFF).any()
+
+
+# ------------------------------------------------------------------------- hand-worked cases
+
+@pytest.mark.parametrize("fixture", ["reduce_hidden8.txt", "rmsnorm_hidden8.txt"])
+@pytest.mark.parametrize("path", [1, 2])
+def test_golden_cases_on_gpu(fixture, path):
+    for case in golden_cases.load(fixture):
+        announce(f"golden {case['name']} path={path}")
+        p = synth.Problem(case["inputs"], case["residual"], case["weight"], case["eps"])
+        ro, out = run_gpu(p, path)
+        assert np.array_equal(ro, case["expect_residual_out"]), case["name"]
+        if "expect_out" in case:
+            assert np.array_equal(out, case["expect_out"]), (case["name"], out)
+        if "expect_reduced" in case:
+            red = fa.fused_ar_reduce([dev(x) for x in case["inputs"]])
+            torch.cuda.synchronize()
+            assert np.array_equal(host(red), case["expect_reduced"]), case["name"]
+
+
+# ------------------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("n,m,hidden", [
+    (1, 1, 8),        # one pack per row: a 64-thread workgroup with 63 idle lanes
+    (2, 3, 16),
+    (8, 2, 520),      # 65 packs: two waves, the second with one active lane
+    (3, 5, 8184),     # 1023 packs
+    (8, 4, 8192),     # exactly 1024 packs
+    (4, 3, 8200),     # 1025 packs: two packs per thread
+    (5, 2, 16392),    # 2049 packs: four packs per thread, ragged
+    (8, 2, 32768),    # the largest row
+    (7, 11, 2880),    # 360 packs, ragged against 64-lane waves
+])
+@pytest.mark.parametrize("path", [1, 2])
+def test_edge_shapes(n, m, hidden, path):
+    p = synth.make_problem(n, m, hidden, seed=hidden + n, name="edge")
+    check_problem(p, path)
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_in_place_residual(path):
+    p = synth.make_problem(8, 24, 7168, seed=9, name="in-place")
+    announce(f"in place path={path}")
+    ro, out = run_gpu(p, path, in_place=True)
+    want_ro, want_out = oracle_rows(p)
+    assert_parity("in-place", ro, out, want_ro, want_out)
+
+
+def test_zero_rows_and_eps():
+    p = synth.make_problem(8, 40, 2880, seed=10, name="zero rows")
+    for x in p.inputs:
+        x[[0, 13, 39]] = 0
+    p.residual[13] = 0  # a row that is zero all the way through: out = +-0 (sign of the weight)
+    for path in (1, 2):
+        announce(f"zero rows path={path}")
+        ro, out = run_gpu(p, path)
+        want_ro, want_out = oracle_rows(p)
+        assert_parity("zero rows", ro, out, want_ro, want_out)
+        assert np.array_equal(ro[0], p.residual[0]) and np.array_equal(ro[39], p.residual[39])
+        assert np.array_equal(out[13], p.weight & np.uint16(0x8000))
+
+
+def test_large_values_and_ties():
+    """The stress mix: +-3e4 rows, whose sums land on bf16 rounding ties."""
+    p = synth.make_problem(8, 300, 2880, seed=11, dist="stress", name="stress ties")
+    for path in (1, 2):
+        check_problem(p, path)
+
+
+def test_rows_beyond_the_grid():
+    """More rows than the row kernel's grid (2^20 workgroups): the workgroups stride over rows."""
+    m = (1 << 20) + 3
+    p = synth.make_problem(2, m, 8, seed=12, name="row stride")
+    for path in (1, 2):
+        announce(f"row stride path={path}")
+        ro, out = run_gpu(p, path)
+        rows = np.array([0, 1, (1 << 20) - 1, 1 << 20, (1 << 20) + 1, m - 1])
+        want_ro, want_out = oracle_rows(p, rows)
+        assert_parity("row stride", ro[rows], out[rows], want_ro, want_out)
+
+
+def test_empty_problem():
+    x = torch.empty(0, 4096, dtype=torch.bfloat16, device="cuda")
+    w = torch.ones(4096, dtype=torch.bfloat16, device="cuda")
+    ro, out = fa.fused_ar_rmsnorm([x, x], x, w, 1e-6)
+    assert ro.shape == (0, 4096) and out.shape == (0, 4096)
+
+
+def test_rejects_aliasing_out_on_gpu_tensors():
+    p = synth.make_problem(2, 4, 64, seed=13)
+    ins = [dev(x) for x in p.inputs]
+    with pytest.raises(fa.FusedArError) as e:
+        fa.fused_ar_rmsnorm(ins, dev(p.residual), dev(p.weight), 1e-6, out=ins[0])
+    assert e.value.status == fa.ERR_ALIAS
+
+
+# ------------------------------------------------------------------------- repeatability
+
+def test_deterministic():
+    p = synth.make_problem(8, 64, 7168, seed=14)
+    for path in (1, 2):
+        announce(f"determinism path={path}")
+        a = run_gpu(p, path)
+        b = run_gpu(p, path)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_graph_replay_matches_eager():
+    """A chain of calls captured into one graph gives the eager result on every replay, with eager
+    work and synchronisations between replays."""
+    p = synth.make_problem(8, 16, 7168, seed=15)
+    ins = [dev(x) for x in p.inputs]
+    res, w = dev(p.residual), dev(p.weight)
+    ro_e, out_e = fa.fused_ar_rmsnorm(ins, res, w, p.eps, path=1)
+    ro2_e, out2_e = fa.fused_ar_rmsnorm(ins, res, w, p.eps, path=2)
+    torch.cuda.synchronize()
+    ro, out = torch.empty_like(res), torch.empty_like(res)
+    ro2, out2 = torch.empty_like(res), torch.empty_like(res)
+    announce("graph capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(20):
+            fa.fused_ar_rmsnorm(ins, res, w, p.eps, residual_out=ro, out=out, path=1)
+            fa.fused_ar_rmsnorm(ins, res, w, p.eps, residual_out=ro2, out=out2, path=2)
+    for replay in range(4):
+        for t in (ro, out, ro2, out2):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ro.view(torch.int16), ro_e.view(torch.int16)), replay
+        assert torch.equal(out.view(torch.int16), out_e.view(torch.int16)), replay
+        assert torch.equal(ro2.view(torch.int16), ro2_e.view(torch.int16)), replay
+        assert torch.equal(out2.view(torch.int16), out2_e.view(torch.int16)), replay
+    want_ro, want_out = oracle_rows(p)
+    assert_parity("graph", host(ro), host(out), want_ro, want_out)
