@@ -20,7 +20,7 @@ constexpr int kMaxBlock = 1024;
 constexpr unsigned kFlatBlock = 256;              // stage-1 workgroup (aiter PR #3817, 2stage >
                                                   // stage-1 launch config)
 constexpr size_t kFlatMaxGrid = size_t(1) << 22;  // beyond this the flat kernel strides
-constexpr int kRowsMaxGrid = 1 << 20;             // beyond this the row kernel strides
+constexpr int kRowsPerLaunch = 1 << 20;           // taller problems take several launches
 
 struct Span {
     uintptr_t lo, hi;  // [lo, hi)
@@ -39,12 +39,18 @@ bool overlaps(const Span &a, const Span &b) { return a.lo < b.hi && b.lo < a.hi;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Packs per thread and threads per workgroup of the row kernel for a row of `packs` packs: the
-// fewest packs per thread (1, 2 or 4) that fit the row in at most 1024 threads, and the thread
-// count rounded up to whole waves. FUSED_AR_MAX_HIDDEN = 4 * 1024 * 8 elements.
-void row_geometry(int packs, int *ppt, int *threads)
+// Packs per thread and threads per workgroup of the row kernel for m rows of `packs` packs.
+// Few rows (m <= kWideRowsMaxM): one pack per thread where the row fits in 1024 threads, so each
+// thread issues all its loads at once and a row costs one memory round trip (latency). Many rows:
+// at least two packs per thread where rows are wider than 512 packs, i.e. smaller workgroups,
+// more of them resident per CU, and the workgroup barriers of different rows overlap
+// (bandwidth). Packs per thread grow (1, 2, 4) until the row fits in 1024 threads; the thread
+// count is rounded up to whole waves. FUSED_AR_MAX_HIDDEN = 4 * 1024 * 8 elements.
+constexpr int kWideRowsMaxM = 256;
+
+void row_geometry(int packs, int m, int *ppt, int *threads)
 {
-    int k = 1;
+    int k = (m > kWideRowsMaxM && packs > 512) ? 2 : 1;
     while (k < 4 && (packs + k - 1) / k > kMaxBlock)
         k *= 2;
     *ppt = k;
@@ -101,7 +107,9 @@ unsigned flat_grid(size_t total_packs)
     return static_cast<unsigned>(g);
 }
 
-unsigned rows_grid(int m) { return static_cast<unsigned>(m < kRowsMaxGrid ? m : kRowsMaxGrid); }
+unsigned rows_grid(int m) { return static_cast<unsigned>(m < kRowsPerLaunch ? m : kRowsPerLaunch); }
+
+unsigned rows_launches(int m) { return static_cast<unsigned>((m + kRowsPerLaunch - 1) / kRowsPerLaunch); }
 
 int check_scalars(int n, int m, int hidden, float eps, int path, bool bounded_hidden)
 {
@@ -125,12 +133,27 @@ int launch(const void *kernel, unsigned grid, unsigned block, void *args, hipStr
     return e == hipSuccess ? FUSED_AR_OK : static_cast<int>(e);
 }
 
+// One workgroup per row, at most kRowsPerLaunch rows per launch; later launches start
+// kRowsPerLaunch rows further into every [m, hidden] buffer.
 int run_rows(const RowArgs &args, int n, int m, int packs, hipStream_t stream)
 {
     int ppt, threads;
-    row_geometry(packs, &ppt, &threads);
-    RowArgs a = args;
-    return launch(row_kernel(n, ppt), rows_grid(m), threads, &a, stream);
+    row_geometry(packs, m, &ppt, &threads);
+    const void *kernel = row_kernel(n, ppt);
+    for (int first = 0; first < m; first += kRowsPerLaunch) {
+        const int rows = m - first < kRowsPerLaunch ? m - first : kRowsPerLaunch;
+        const size_t skip = (size_t)first * (size_t)packs;  // in packs
+        RowArgs a = args;
+        for (int i = 0; i < n; ++i)
+            a.in[i] += skip;
+        a.residual += skip;
+        a.residual_out += skip;
+        a.out += skip;
+        const int rc = launch(kernel, static_cast<unsigned>(rows), threads, &a, stream);
+        if (rc != FUSED_AR_OK)
+            return rc;
+    }
+    return FUSED_AR_OK;
 }
 
 int run_flat(const fa_bf16 *const *inputs, int n, size_t total_packs, fa_bf16 *reduced,
@@ -218,7 +241,6 @@ extern "C" int fused_ar_rmsnorm(const fa_bf16 *const *inputs, int n, const fa_bf
     a.eps = eps;
     a.hidden = static_cast<float>(hidden);
     a.packs = packs;
-    a.rows = m;
 
     if (path == FUSED_AR_PATH_ONESTAGE) {
         for (int i = 0; i < n; ++i)
@@ -283,11 +305,12 @@ extern "C" int fused_ar_describe_launch(int n, int m, int hidden, int path,
         return FUSED_AR_OK;
     const int packs = hidden / kPackElems;
     int ppt, threads;
-    row_geometry(packs, &ppt, &threads);
+    row_geometry(packs, m, &ppt, &threads);
     fused_ar_kernel_launch rows{};
     rows.grid = rows_grid(m);
     rows.block = static_cast<unsigned>(threads);
     rows.per_thread = static_cast<unsigned>(ppt);
+    rows.launches = rows_launches(m);
     if (path == FUSED_AR_PATH_ONESTAGE) {
         plan->kernels = 1;
         strcpy(rows.name, "onestage");
@@ -301,6 +324,7 @@ extern "C" int fused_ar_describe_launch(int n, int m, int hidden, int path,
         flat.block = kFlatBlock;
         const size_t covered = (size_t)flat.grid * kFlatBlock;
         flat.per_thread = static_cast<unsigned>((total + covered - 1) / covered);
+        flat.launches = 1;
         strcpy(rows.name, "stage2_norm");
         plan->launch[0] = flat;
         plan->launch[1] = rows;

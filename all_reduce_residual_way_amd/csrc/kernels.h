@@ -33,7 +33,6 @@ struct RowArgs {
     float eps;
     float hidden;                 // row length as a float, the divisor of the mean
     int packs;                    // packs per row = hidden / 8
-    int rows;                     // m
 };
 
 struct FlatArgs {
@@ -53,88 +52,92 @@ __device__ __forceinline__ F8 reduce_packs(const u32x4 (&x)[N])
     return acc;
 }
 
-// A pack at a byte offset from a wave-uniform base: the base stays in scalar registers and the
-// per-lane offset is 32 bits, which lets the loads and stores use scalar-base addressing instead
-// of a 64-bit address per lane per buffer.
+// A pack at a byte offset from a wave-uniform base (the base stays in scalar registers, the
+// per-lane offset is 32 bits). load_pack is an ordinary load, for data that is reused (the
+// weight, read by every row); load_stream is a non-temporal load, for data read exactly once
+// (the partial sums and the residual), so that the stream does not displace reused lines.
+// store_stream is a non-temporal store: nothing this library writes is read back soon enough
+// to profit from staying in the caches.
 __device__ __forceinline__ u32x4 load_pack(const char *base, uint32_t off)
 {
     return *reinterpret_cast<const u32x4 *>(base + off);
 }
 
-__device__ __forceinline__ void store_pack(char *base, uint32_t off, u32x4 v)
+__device__ __forceinline__ u32x4 load_stream(const char *base, uint32_t off)
 {
-    *reinterpret_cast<u32x4 *>(base + off) = v;
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + off));
 }
 
-// One workgroup handles rows blockIdx.x, blockIdx.x + gridDim.x, ...; thread t handles packs
-// t, t + blockDim.x, ..., PPT of them, of each row. For each of its packs a thread loads the N
-// inputs and the residual, reduces, writes residual_out and accumulates the square-sum, keeping
-// only the bf16 residual_out pack; one workgroup reduction then gives the row statistic and the
-// normalised row is written from those registers.
+__device__ __forceinline__ void store_stream(char *base, uint32_t off, u32x4 v)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(base + off));
+}
+
+// Workgroup b handles row b (the host launches one workgroup per row, splitting very tall
+// problems into several launches); thread t handles packs t, t + blockDim.x, ..., PPT of them.
+// For each of its packs a thread loads the N inputs, the residual and the weight, reduces,
+// writes residual_out and accumulates the square-sum, keeping only the bf16 residual_out and
+// weight packs; one workgroup reduction then gives the row statistic and the normalised row is
+// written from those registers.
 template <int N, int PPT>
 __global__ void __launch_bounds__(1024) k_rows(RowArgs a)
 {
-    __shared__ float slots[2][kMaxWaves];  // alternate per row, so one barrier per row suffices
+    __shared__ float slots[kMaxWaves];
     const uint32_t tid = threadIdx.x;
     const uint32_t nthreads = blockDim.x;
     const uint32_t packs = (uint32_t)a.packs;
+    const size_t row_bytes = (size_t)blockIdx.x * packs * sizeof(u32x4);
     const char *weight = reinterpret_cast<const char *>(a.weight);
-    int parity = 0;
+    const char *in[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        in[i] = reinterpret_cast<const char *>(a.in[i]) + row_bytes;
+    const char *residual = reinterpret_cast<const char *>(a.residual) + row_bytes;
+    char *residual_out = reinterpret_cast<char *>(a.residual_out) + row_bytes;
+    char *out = reinterpret_cast<char *>(a.out) + row_bytes;
 
-    for (int row = blockIdx.x; row < a.rows; row += gridDim.x) {
-        const size_t row_bytes = (size_t)row * packs * sizeof(u32x4);
-        const char *in[N];
+    u32x4 ro[PPT];
+    u32x4 w[PPT];
+    float ss = 0.0f;
 #pragma unroll
-        for (int i = 0; i < N; ++i)
-            in[i] = reinterpret_cast<const char *>(a.in[i]) + row_bytes;
-        const char *residual = reinterpret_cast<const char *>(a.residual) + row_bytes;
-        char *residual_out = reinterpret_cast<char *>(a.residual_out) + row_bytes;
-        char *out = reinterpret_cast<char *>(a.out) + row_bytes;
-
-        u32x4 ro[PPT];
-        u32x4 w[PPT];
-        float ss = 0.0f;
+    for (int k = 0; k < PPT; ++k) {
+        const uint32_t p = tid + k * nthreads;
+        if (p < packs) {
+            const uint32_t off = p * (uint32_t)sizeof(u32x4);
+            u32x4 x[N];
 #pragma unroll
-        for (int k = 0; k < PPT; ++k) {
-            const uint32_t p = tid + k * nthreads;
-            if (p < packs) {
-                const uint32_t off = p * (uint32_t)sizeof(u32x4);
-                u32x4 x[N];
+            for (int i = 0; i < N; ++i)
+                x[i] = load_stream(in[i], off);
+            const u32x4 res = load_stream(residual, off);
+            w[k] = load_pack(weight, off);
+            // all of this slot's loads are in flight before any arithmetic waits on one
+            __builtin_amdgcn_sched_barrier(0);
+            F8 sum = widen(narrow(reduce_packs<N>(x)));  // the reduced value, in bf16
+            add_into(sum, widen(res));
+            ro[k] = narrow(sum);
+            store_stream(residual_out, off, ro[k]);
+            const F8 y = widen(ro[k]);
 #pragma unroll
-                for (int i = 0; i < N; ++i)
-                    x[i] = load_pack(in[i], off);
-                const u32x4 res = load_pack(residual, off);
-                w[k] = load_pack(weight, off);
-                // all of this slot's loads are in flight before any arithmetic waits on one
-                __builtin_amdgcn_sched_barrier(0);
-                F8 sum = widen(narrow(reduce_packs<N>(x)));  // the reduced value, in bf16
-                add_into(sum, widen(res));
-                ro[k] = narrow(sum);
-                store_pack(residual_out, off, ro[k]);
-                const F8 y = widen(ro[k]);
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    ss = __builtin_fmaf(y.v[e], y.v[e], ss);  // y * y is exact in fp32
-            }
+            for (int e = 0; e < 8; ++e)
+                ss = __builtin_fmaf(y.v[e], y.v[e], ss);  // y * y is exact in fp32
         }
+    }
 
-        const float total = block_sum(ss, slots[parity]);
-        parity ^= 1;
-        const float rstd = 1.0f / __builtin_sqrtf(total / a.hidden + a.eps);
+    const float total = block_sum(ss, slots);
+    const float rstd = 1.0f / __builtin_sqrtf(total / a.hidden + a.eps);
 
 #pragma unroll
-        for (int k = 0; k < PPT; ++k) {
-            const uint32_t p = tid + k * nthreads;
-            if (p < packs) {
-                const uint32_t off = p * (uint32_t)sizeof(u32x4);
-                const F8 y = widen(ro[k]);
-                const F8 g = widen(w[k]);
-                F8 o;
+    for (int k = 0; k < PPT; ++k) {
+        const uint32_t p = tid + k * nthreads;
+        if (p < packs) {
+            const uint32_t off = p * (uint32_t)sizeof(u32x4);
+            const F8 y = widen(ro[k]);
+            const F8 g = widen(w[k]);
+            F8 o;
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    o.v[e] = (y.v[e] * rstd) * g.v[e];
-                store_pack(out, off, narrow(o));
-            }
+            for (int e = 0; e < 8; ++e)
+                o.v[e] = (y.v[e] * rstd) * g.v[e];
+            store_stream(out, off, narrow(o));
         }
     }
 }
@@ -154,9 +157,9 @@ __global__ void __launch_bounds__(1024) k_flat_reduce(FlatArgs a)
         u32x4 x[N];
 #pragma unroll
         for (int i = 0; i < N; ++i)
-            x[i] = load_pack(reinterpret_cast<const char *>(a.in[i]) + bytes, off);
+            x[i] = load_stream(reinterpret_cast<const char *>(a.in[i]) + bytes, off);
         __builtin_amdgcn_sched_barrier(0);  // all N loads in flight before the first add
-        store_pack(reinterpret_cast<char *>(a.out) + bytes, off, narrow(reduce_packs<N>(x)));
+        store_stream(reinterpret_cast<char *>(a.out) + bytes, off, narrow(reduce_packs<N>(x)));
     }
 }
 

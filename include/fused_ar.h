@@ -126,9 +126,11 @@ int fused_ar_auto_path(int n, int m, int hidden);
 /* One kernel launch of a call, as fused_ar_describe_launch reports it. */
 typedef struct {
     char name[32];        /* kernel name: "onestage", "stage1_reduce" or "stage2_norm" */
-    unsigned grid;        /* workgroups */
+    unsigned grid;        /* workgroups per launch (the row kernels: one per row) */
     unsigned block;       /* threads per workgroup (a multiple of 64) */
     unsigned per_thread;  /* 8-element packs each thread handles per row (or per stride) */
+    unsigned launches;    /* launches of this kernel per call (rows come in launches of at most
+                             2^20 workgroups) */
 } fused_ar_kernel_launch;
 
 typedef struct {

@@ -162,6 +162,19 @@ def test_launch_geometry_covers_each_row(hidden):
             assert flat["grid"] * flat["block"] * flat["per_thread"] >= 100 * packs
 
 
+def test_launch_geometry_by_row_count():
+    # few rows: one pack per thread (a row in one memory round trip); many rows: two packs per
+    # thread for rows wider than 512 packs; rows come in launches of at most 2^20 workgroups
+    k = fa.describe_launch(8, 256, 7168, 1)["kernels"][0]
+    assert (k["per_thread"], k["block"], k["launches"]) == (1, 896, 1)
+    k = fa.describe_launch(8, 257, 7168, 1)["kernels"][0]
+    assert (k["per_thread"], k["block"]) == (2, 448)
+    k = fa.describe_launch(8, 4096, 2880, 1)["kernels"][0]
+    assert (k["per_thread"], k["block"]) == (1, 384)
+    k = fa.describe_launch(2, (1 << 20) + 3, 8, 2)["kernels"][1]
+    assert (k["grid"], k["launches"]) == (1 << 20, 2)
+
+
 def test_launch_geometry_auto_and_empty():
     assert fa.describe_launch(8, 16, 7168)["path"] == 1
     assert fa.describe_launch(8, 17, 7168)["path"] == 2

@@ -242,8 +242,17 @@ def test_large_values_and_ties():
         check_problem(p, path)
 
 
+@pytest.mark.parametrize("m", [256, 257])
+def test_both_row_geometries(m):
+    """Either side of the row count where the row kernel switches from one to two packs per
+    thread (hidden = 7168)."""
+    p = synth.make_problem(8, m, 7168, seed=16, name="geometry")
+    for path in (1, 2):
+        check_problem(p, path)
+
+
 def test_rows_beyond_the_grid():
-    """More rows than the row kernel's grid (2^20 workgroups): the workgroups stride over rows."""
+    """More rows than one launch takes (2^20 workgroups): the rows come in two launches."""
     m = (1 << 20) + 3
     p = synth.make_problem(2, m, 8, seed=12, name="row stride")
     for path in (1, 2):
