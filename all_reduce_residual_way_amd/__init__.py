@@ -12,17 +12,22 @@ import ctypes
 import os
 
 __all__ = [
-    "FusedArError", "library", "fused_ar_rmsnorm", "fused_ar_reduce", "fused_ar_rmsnorm_ptrs",
-    "fused_ar_reduce_ptrs", "fused_ar_rmsnorm_check_ptrs", "auto_path", "describe_launch", "strerror",
+    "FusedArError", "Options", "library", "fused_ar_rmsnorm", "fused_ar_unfused_rmsnorm",
+    "fused_ar_reduce", "fused_ar_rmsnorm_ptrs", "fused_ar_rmsnorm_ex_ptrs",
+    "fused_ar_unfused_rmsnorm_ptrs", "fused_ar_reduce_ptrs", "fused_ar_rmsnorm_check_ptrs",
+    "auto_path", "describe_launch", "strerror",
     "OK", "ERR_INVALID", "ERR_SHAPE", "ERR_ALIGN", "ERR_ALIAS",
-    "PATH_AUTO", "PATH_ONESTAGE", "PATH_TWOSTAGE", "MAX_INPUTS", "MAX_HIDDEN",
+    "PATH_AUTO", "PATH_ONESTAGE", "PATH_TWOSTAGE", "PATH_UNFUSED", "WAVE_DPP", "WAVE_BPERMUTE",
+    "STAGE1_FLAT", "STAGE1_LDS", "MAX_INPUTS", "MAX_HIDDEN",
 ]
 
 LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfused_ar.so")
 
 # Values of include/fused_ar.h.
 OK, ERR_INVALID, ERR_SHAPE, ERR_ALIGN, ERR_ALIAS = 0, -1, -2, -3, -4
-PATH_AUTO, PATH_ONESTAGE, PATH_TWOSTAGE = 0, 1, 2
+PATH_AUTO, PATH_ONESTAGE, PATH_TWOSTAGE, PATH_UNFUSED = 0, 1, 2, 3
+WAVE_DPP, WAVE_BPERMUTE = 0, 1
+STAGE1_FLAT, STAGE1_LDS = 0, 1
 MAX_INPUTS, MAX_HIDDEN = 8, 32768
 
 _VP = ctypes.c_void_p
@@ -34,7 +39,13 @@ class _KernelLaunch(ctypes.Structure):
 
 
 class _LaunchPlan(ctypes.Structure):
-    _fields_ = [("path", ctypes.c_int), ("kernels", ctypes.c_int), ("launch", _KernelLaunch * 2)]
+    _fields_ = [("path", ctypes.c_int), ("kernels", ctypes.c_int), ("launch", _KernelLaunch * 3)]
+
+
+class Options(ctypes.Structure):
+    """fused_ar_options: alternative kernel designs (see include/fused_ar.h)."""
+    _fields_ = [("wave_reduce", ctypes.c_int), ("stage1", ctypes.c_int),
+                ("stage1_block", ctypes.c_int), ("packs_per_thread", ctypes.c_int)]
 
 
 class FusedArError(RuntimeError):
@@ -61,6 +72,18 @@ def library():
         lib.fused_ar_rmsnorm.argtypes = [ctypes.POINTER(_VP), ctypes.c_int, _VP, _VP, ctypes.c_float,
                                          ctypes.c_int, ctypes.c_int, _VP, _VP, ctypes.c_int, _VP]
         lib.fused_ar_rmsnorm.restype = ctypes.c_int
+        lib.fused_ar_rmsnorm_ex.argtypes = [ctypes.POINTER(_VP), ctypes.c_int, _VP, _VP,
+                                            ctypes.c_float, ctypes.c_int, ctypes.c_int, _VP, _VP,
+                                            ctypes.c_int, ctypes.POINTER(Options), _VP]
+        lib.fused_ar_rmsnorm_ex.restype = ctypes.c_int
+        lib.fused_ar_unfused_rmsnorm.argtypes = [ctypes.POINTER(_VP), ctypes.c_int, _VP, _VP,
+                                                 ctypes.c_float, ctypes.c_int, ctypes.c_int, _VP,
+                                                 _VP, _VP]
+        lib.fused_ar_unfused_rmsnorm.restype = ctypes.c_int
+        lib.fused_ar_describe_launch_ex.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                    ctypes.c_int, ctypes.POINTER(Options),
+                                                    ctypes.POINTER(_LaunchPlan)]
+        lib.fused_ar_describe_launch_ex.restype = ctypes.c_int
         lib.fused_ar_rmsnorm_check.argtypes = [ctypes.POINTER(_VP), ctypes.c_int, _VP, _VP,
                                                ctypes.c_float, ctypes.c_int, ctypes.c_int, _VP,
                                                _VP, ctypes.c_int]
@@ -88,11 +111,12 @@ def auto_path(n, m, hidden):
     return library().fused_ar_auto_path(int(n), int(m), int(hidden))
 
 
-def describe_launch(n, m, hidden, path=PATH_AUTO):
+def describe_launch(n, m, hidden, path=PATH_AUTO, options=None):
     """Kernels, grids and workgroup sizes of a call, as a dict; raises on bad arguments."""
     plan = _LaunchPlan()
-    rc = library().fused_ar_describe_launch(int(n), int(m), int(hidden), int(path),
-                                            ctypes.byref(plan))
+    opt = ctypes.byref(options) if options is not None else None
+    rc = library().fused_ar_describe_launch_ex(int(n), int(m), int(hidden), int(path), opt,
+                                               ctypes.byref(plan))
     if rc != OK:
         raise FusedArError(rc, "fused_ar_describe_launch")
     return {
@@ -117,6 +141,25 @@ def fused_ar_rmsnorm_ptrs(input_ptrs, residual, weight, eps, m, hidden, residual
     return library().fused_ar_rmsnorm(arr, len(input_ptrs), _VP(residual), _VP(weight),
                                       float(eps), int(m), int(hidden), _VP(residual_out), _VP(out),
                                       int(path), _VP(stream))
+
+
+def fused_ar_rmsnorm_ex_ptrs(input_ptrs, residual, weight, eps, m, hidden, residual_out, out,
+                             path=PATH_AUTO, options=None, stream=0):
+    """Raw call of fused_ar_rmsnorm_ex; ``options`` is an Options or None; returns the status."""
+    arr = _ptr_array(input_ptrs)
+    opt = ctypes.byref(options) if options is not None else None
+    return library().fused_ar_rmsnorm_ex(arr, len(input_ptrs), _VP(residual), _VP(weight),
+                                         float(eps), int(m), int(hidden), _VP(residual_out),
+                                         _VP(out), int(path), opt, _VP(stream))
+
+
+def fused_ar_unfused_rmsnorm_ptrs(input_ptrs, residual, weight, eps, m, hidden, residual_out,
+                                  out, stream=0):
+    """Raw call of the unfused three-kernel sequence; returns the status."""
+    arr = _ptr_array(input_ptrs)
+    return library().fused_ar_unfused_rmsnorm(arr, len(input_ptrs), _VP(residual), _VP(weight),
+                                              float(eps), int(m), int(hidden), _VP(residual_out),
+                                              _VP(out), _VP(stream))
 
 
 def fused_ar_rmsnorm_check_ptrs(input_ptrs, residual, weight, eps, m, hidden, residual_out, out,
@@ -156,26 +199,7 @@ def _stream_handle(stream, device):
     return stream.cuda_stream
 
 
-def fused_ar_rmsnorm(inputs, residual, weight, eps=1e-6, *, residual_out=None, out=None,
-                     path=PATH_AUTO, stream=None):
-    """The fused epilogue on one GPU.
-
-    Args:
-        inputs: list of n (1..8) bf16 CUDA tensors of shape (m, hidden), the partial sums; they
-            are reduced in fp32 in list order.
-        residual: bf16 (m, hidden). weight: bf16 (hidden,). eps: float >= 0.
-        residual_out: optional bf16 (m, hidden) output buffer; may be ``residual`` itself.
-        out: optional bf16 (m, hidden) output buffer, overlapping nothing else (the two-stage path
-            also uses it as scratch).
-        path: 0 automatic, 1 one-stage, 2 two-stage.
-        stream: torch.cuda.Stream to enqueue on (default: the current stream).
-    Returns:
-        (residual_out, out). Missing outputs are allocated with ``torch.empty_like(residual)``
-        and belong to the caller. The work is asynchronous on the stream.
-    Raises:
-        TypeError/ValueError for tensors of the wrong dtype, device, shape or layout;
-        FusedArError for a non-zero library status.
-    """
+def _prepare(inputs, residual, weight, residual_out, out):
     import torch
     if not isinstance(inputs, (list, tuple)) or not inputs:
         raise ValueError("inputs must be a non-empty list of tensors")
@@ -193,11 +217,49 @@ def fused_ar_rmsnorm(inputs, residual, weight, eps=1e-6, *, residual_out=None, o
         out = torch.empty_like(residual)
     _check_tensor(residual_out, "residual_out", (m, hidden), device)
     _check_tensor(out, "out", (m, hidden), device)
-    rc = fused_ar_rmsnorm_ptrs([x.data_ptr() for x in inputs], residual.data_ptr(),
-                               weight.data_ptr(), eps, m, hidden, residual_out.data_ptr(),
-                               out.data_ptr(), path, _stream_handle(stream, device))
+    return m, hidden, device, residual_out, out
+
+
+def fused_ar_rmsnorm(inputs, residual, weight, eps=1e-6, *, residual_out=None, out=None,
+                     path=PATH_AUTO, stream=None, options=None):
+    """The fused epilogue on one GPU.
+
+    Args:
+        inputs: list of n (1..8) bf16 CUDA tensors of shape (m, hidden), the partial sums; they
+            are reduced in fp32 in list order.
+        residual: bf16 (m, hidden). weight: bf16 (hidden,). eps: float >= 0.
+        residual_out: optional bf16 (m, hidden) output buffer; may be ``residual`` itself.
+        out: optional bf16 (m, hidden) output buffer, overlapping nothing else (the two-stage path
+            also uses it as scratch).
+        path: 0 automatic, 1 one-stage, 2 two-stage (3: the unfused three-kernel sequence).
+        stream: torch.cuda.Stream to enqueue on (default: the current stream).
+        options: an Options (alternative kernel designs) or None for the defaults.
+    Returns:
+        (residual_out, out). Missing outputs are allocated with ``torch.empty_like(residual)``
+        and belong to the caller. The work is asynchronous on the stream.
+    Raises:
+        TypeError/ValueError for tensors of the wrong dtype, device, shape or layout;
+        FusedArError for a non-zero library status.
+    """
+    m, hidden, device, residual_out, out = _prepare(inputs, residual, weight, residual_out, out)
+    rc = fused_ar_rmsnorm_ex_ptrs([x.data_ptr() for x in inputs], residual.data_ptr(),
+                                  weight.data_ptr(), eps, m, hidden, residual_out.data_ptr(),
+                                  out.data_ptr(), path, options, _stream_handle(stream, device))
     if rc != OK:
         raise FusedArError(rc, "fused_ar_rmsnorm")
+    return residual_out, out
+
+
+def fused_ar_unfused_rmsnorm(inputs, residual, weight, eps=1e-6, *, residual_out=None, out=None,
+                             stream=None):
+    """The same result as fused_ar_rmsnorm, computed as three kernels (reduce, residual add,
+    RMSNorm): the unfused baseline. Arguments and returns as fused_ar_rmsnorm (no path)."""
+    m, hidden, device, residual_out, out = _prepare(inputs, residual, weight, residual_out, out)
+    rc = fused_ar_unfused_rmsnorm_ptrs([x.data_ptr() for x in inputs], residual.data_ptr(),
+                                       weight.data_ptr(), eps, m, hidden, residual_out.data_ptr(),
+                                       out.data_ptr(), _stream_handle(stream, device))
+    if rc != OK:
+        raise FusedArError(rc, "fused_ar_unfused_rmsnorm")
     return residual_out, out
 
 

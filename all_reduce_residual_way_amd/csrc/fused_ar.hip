@@ -1,5 +1,5 @@
-// fused_ar.hip - host side of libfused_ar.so: argument checks, path choice, launch geometry and
-// the extern "C" entry points declared in include/fused_ar.h.
+// fused_ar.hip - host side of libfused_ar.so: argument checks, path choice, launch plans and the
+// extern "C" entry points declared in include/fused_ar.h.
 #include "fused_ar.h"
 
 #include <hip/hip_runtime.h>
@@ -14,6 +14,7 @@ namespace {
 
 using fa::FlatArgs;
 using fa::RowArgs;
+using fa::u32x4;
 
 constexpr int kPackElems = 8;
 constexpr int kMaxBlock = 1024;
@@ -21,6 +22,9 @@ constexpr unsigned kFlatBlock = 256;              // stage-1 workgroup (aiter PR
                                                   // stage-1 launch config)
 constexpr size_t kFlatMaxGrid = size_t(1) << 22;  // beyond this the flat kernel strides
 constexpr int kRowsPerLaunch = 1 << 20;           // taller problems take several launches
+constexpr int kPathUnfusedPlan = 3;               // internal plan id of the unfused sequence
+
+// ------------------------------------------------------------------------------------ checks
 
 struct Span {
     uintptr_t lo, hi;  // [lo, hi)
@@ -39,78 +43,6 @@ bool overlaps(const Span &a, const Span &b) { return a.lo < b.hi && b.lo < a.hi;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Packs per thread and threads per workgroup of the row kernel for m rows of `packs` packs.
-// Few rows (m <= kWideRowsMaxM): one pack per thread where the row fits in 1024 threads, so each
-// thread issues all its loads at once and a row costs one memory round trip (latency). Many rows:
-// at least two packs per thread where rows are wider than 512 packs, i.e. smaller workgroups,
-// more of them resident per CU, and the workgroup barriers of different rows overlap
-// (bandwidth). Packs per thread grow (1, 2, 4) until the row fits in 1024 threads; the thread
-// count is rounded up to whole waves. FUSED_AR_MAX_HIDDEN = 4 * 1024 * 8 elements.
-constexpr int kWideRowsMaxM = 256;
-
-void row_geometry(int packs, int m, int *ppt, int *threads)
-{
-    int k = (m > kWideRowsMaxM && packs > 512) ? 2 : 1;
-    while (k < 4 && (packs + k - 1) / k > kMaxBlock)
-        k *= 2;
-    *ppt = k;
-    const int t = (packs + k - 1) / k;
-    *threads = (t + 63) / 64 * 64;
-}
-
-template <int N>
-const void *row_kernel_n(int ppt)
-{
-    switch (ppt) {
-    case 1: return reinterpret_cast<const void *>(&fa::k_rows<N, 1>);
-    case 2: return reinterpret_cast<const void *>(&fa::k_rows<N, 2>);
-    case 4: return reinterpret_cast<const void *>(&fa::k_rows<N, 4>);
-    default: return nullptr;
-    }
-}
-
-const void *row_kernel(int n, int ppt)
-{
-    switch (n) {
-    case 1: return row_kernel_n<1>(ppt);
-    case 2: return row_kernel_n<2>(ppt);
-    case 3: return row_kernel_n<3>(ppt);
-    case 4: return row_kernel_n<4>(ppt);
-    case 5: return row_kernel_n<5>(ppt);
-    case 6: return row_kernel_n<6>(ppt);
-    case 7: return row_kernel_n<7>(ppt);
-    case 8: return row_kernel_n<8>(ppt);
-    default: return nullptr;
-    }
-}
-
-const void *flat_kernel(int n)
-{
-    switch (n) {
-    case 1: return reinterpret_cast<const void *>(&fa::k_flat_reduce<1>);
-    case 2: return reinterpret_cast<const void *>(&fa::k_flat_reduce<2>);
-    case 3: return reinterpret_cast<const void *>(&fa::k_flat_reduce<3>);
-    case 4: return reinterpret_cast<const void *>(&fa::k_flat_reduce<4>);
-    case 5: return reinterpret_cast<const void *>(&fa::k_flat_reduce<5>);
-    case 6: return reinterpret_cast<const void *>(&fa::k_flat_reduce<6>);
-    case 7: return reinterpret_cast<const void *>(&fa::k_flat_reduce<7>);
-    case 8: return reinterpret_cast<const void *>(&fa::k_flat_reduce<8>);
-    default: return nullptr;
-    }
-}
-
-unsigned flat_grid(size_t total_packs)
-{
-    size_t g = (total_packs + kFlatBlock - 1) / kFlatBlock;
-    if (g > kFlatMaxGrid)
-        g = kFlatMaxGrid;
-    return static_cast<unsigned>(g);
-}
-
-unsigned rows_grid(int m) { return static_cast<unsigned>(m < kRowsPerLaunch ? m : kRowsPerLaunch); }
-
-unsigned rows_launches(int m) { return static_cast<unsigned>((m + kRowsPerLaunch - 1) / kRowsPerLaunch); }
-
 int check_scalars(int n, int m, int hidden, float eps, int path, bool bounded_hidden)
 {
     if (n < 1 || n > FUSED_AR_MAX_INPUTS || m < 0 || hidden <= 0)
@@ -126,66 +58,11 @@ int check_scalars(int n, int m, int hidden, float eps, int path, bool bounded_hi
     return FUSED_AR_OK;
 }
 
-int launch(const void *kernel, unsigned grid, unsigned block, void *args, hipStream_t stream)
+// The pointer checks of fused_ar_rmsnorm (m > 0): nulls, alignment, forbidden overlaps.
+int check_buffers(const fa_bf16 *const *inputs, int n, const fa_bf16 *residual,
+                  const fa_bf16 *weight, int m, int hidden, const fa_bf16 *residual_out,
+                  const fa_bf16 *out)
 {
-    void *params[] = {args};
-    const hipError_t e = hipLaunchKernel(kernel, dim3(grid), dim3(block), params, 0, stream);
-    return e == hipSuccess ? FUSED_AR_OK : static_cast<int>(e);
-}
-
-// One workgroup per row, at most kRowsPerLaunch rows per launch; later launches start
-// kRowsPerLaunch rows further into every [m, hidden] buffer.
-int run_rows(const RowArgs &args, int n, int m, int packs, hipStream_t stream)
-{
-    int ppt, threads;
-    row_geometry(packs, m, &ppt, &threads);
-    const void *kernel = row_kernel(n, ppt);
-    for (int first = 0; first < m; first += kRowsPerLaunch) {
-        const int rows = m - first < kRowsPerLaunch ? m - first : kRowsPerLaunch;
-        const size_t skip = (size_t)first * (size_t)packs;  // in packs
-        RowArgs a = args;
-        for (int i = 0; i < n; ++i)
-            a.in[i] += skip;
-        a.residual += skip;
-        a.residual_out += skip;
-        a.out += skip;
-        const int rc = launch(kernel, static_cast<unsigned>(rows), threads, &a, stream);
-        if (rc != FUSED_AR_OK)
-            return rc;
-    }
-    return FUSED_AR_OK;
-}
-
-int run_flat(const fa_bf16 *const *inputs, int n, size_t total_packs, fa_bf16 *reduced,
-             hipStream_t stream)
-{
-    FlatArgs a{};
-    for (int i = 0; i < n; ++i)
-        a.in[i] = reinterpret_cast<const fa::u32x4 *>(inputs[i]);
-    a.out = reinterpret_cast<fa::u32x4 *>(reduced);
-    a.total_packs = total_packs;
-    return launch(flat_kernel(n), flat_grid(total_packs), kFlatBlock, &a, stream);
-}
-
-}  // namespace
-
-extern "C" int fused_ar_auto_path(int n, int m, int hidden)
-{
-    (void)hidden;
-    if (n < 1 || n > FUSED_AR_MAX_INPUTS || m < 0)
-        return FUSED_AR_ERR_INVALID;
-    const int one_stage_max_m = n <= 4 ? 32 : 16;
-    return m <= one_stage_max_m ? FUSED_AR_PATH_ONESTAGE : FUSED_AR_PATH_TWOSTAGE;
-}
-
-extern "C" int fused_ar_rmsnorm_check(const fa_bf16 *const *inputs, int n,
-                                      const fa_bf16 *residual, const fa_bf16 *weight, float eps,
-                                      int m, int hidden, const fa_bf16 *residual_out,
-                                      const fa_bf16 *out, int path)
-{
-    int rc = check_scalars(n, m, hidden, eps, path, true);
-    if (rc != FUSED_AR_OK || m == 0)
-        return rc;
     if (inputs == nullptr || residual == nullptr || weight == nullptr || residual_out == nullptr ||
         out == nullptr)
         return FUSED_AR_ERR_INVALID;
@@ -220,41 +97,352 @@ extern "C" int fused_ar_rmsnorm_check(const fa_bf16 *const *inputs, int n,
     return FUSED_AR_OK;
 }
 
-extern "C" int fused_ar_rmsnorm(const fa_bf16 *const *inputs, int n, const fa_bf16 *residual,
-                                const fa_bf16 *weight, float eps, int m, int hidden,
-                                fa_bf16 *residual_out, fa_bf16 *out, int path, hipStream_t stream)
+// ------------------------------------------------------------------------------------ plans
+
+struct Options {
+    bool bpermute;        // wave reduction by ds_bpermute instead of DPP
+    bool lds_stage1;      // LDS-staged wave-per-input stage 1 instead of the flat reduce
+    unsigned flat_block;  // workgroup of the flat kernels
+    int ppt;              // packs per thread of the row kernels; 0 = automatic
+};
+
+constexpr Options kDefaultOptions = {false, false, kFlatBlock, 0};
+
+int read_options(const fused_ar_options *o, Options *out)
 {
-    int rc = fused_ar_rmsnorm_check(inputs, n, residual, weight, eps, m, hidden, residual_out, out,
-                                    path);
-    if (rc != FUSED_AR_OK || m == 0)
-        return rc;
+    *out = kDefaultOptions;
+    if (o == nullptr)
+        return FUSED_AR_OK;
+    if ((o->wave_reduce != FUSED_AR_WAVE_DPP && o->wave_reduce != FUSED_AR_WAVE_BPERMUTE) ||
+        (o->stage1 != FUSED_AR_STAGE1_FLAT && o->stage1 != FUSED_AR_STAGE1_LDS))
+        return FUSED_AR_ERR_INVALID;
+    if (o->stage1_block != 0 &&
+        (o->stage1_block < 64 || o->stage1_block > kMaxBlock || o->stage1_block % 64 != 0))
+        return FUSED_AR_ERR_INVALID;
+    if (o->packs_per_thread != 0 && o->packs_per_thread != 1 && o->packs_per_thread != 2 &&
+        o->packs_per_thread != 4)
+        return FUSED_AR_ERR_INVALID;
+    out->bpermute = o->wave_reduce == FUSED_AR_WAVE_BPERMUTE;
+    out->lds_stage1 = o->stage1 == FUSED_AR_STAGE1_LDS;
+    out->flat_block = o->stage1_block != 0 ? static_cast<unsigned>(o->stage1_block) : kFlatBlock;
+    out->ppt = o->packs_per_thread;
+    return FUSED_AR_OK;
+}
 
-    if (path == FUSED_AR_PATH_AUTO)
-        path = fused_ar_auto_path(n, m, hidden);
+// Packs per thread and threads per workgroup of the row kernel for m rows of `packs` packs.
+// One pack per thread where the row fits in 1024 threads: each thread issues all its loads at
+// once and a row costs one memory round trip. Exception, from measurements on MI355X (N = 4 and
+// 8, hidden 4096-8192): for 256 < m <= 1024 rows wider than 512 packs, two packs per thread
+// (half-size workgroups, twice as many resident per CU) are up to 7 % faster; elsewhere one pack
+// per thread is as fast or up to 4 % faster. Packs per thread grow (1, 2, 4) until the row fits
+// in 1024 threads; the thread count is rounded up to whole waves.
+// FUSED_AR_MAX_HIDDEN = 4 * 1024 * 8 elements.
+constexpr int kTwoPackMinM = 257;
+constexpr int kTwoPackMaxM = 1024;
 
+int row_geometry(int packs, int m, int forced_ppt, int *ppt, int *threads)
+{
+    int k = forced_ppt;
+    if (k == 0) {
+        k = (m >= kTwoPackMinM && m <= kTwoPackMaxM && packs > 512) ? 2 : 1;
+        while (k < 4 && (packs + k - 1) / k > kMaxBlock)
+            k *= 2;
+    } else if ((packs + k - 1) / k > kMaxBlock) {
+        return FUSED_AR_ERR_SHAPE;  // the requested packs per thread do not fit the row
+    }
+    *ppt = k;
+    const int t = (packs + k - 1) / k;
+    *threads = (t + 63) / 64 * 64;
+    return FUSED_AR_OK;
+}
+
+template <int N, bool kB, bool kR>
+const void *row_kernel_np(int ppt)
+{
+    switch (ppt) {
+    case 1: return reinterpret_cast<const void *>(&fa::k_rows<N, 1, kB, kR>);
+    case 2: return reinterpret_cast<const void *>(&fa::k_rows<N, 2, kB, kR>);
+    case 4: return reinterpret_cast<const void *>(&fa::k_rows<N, 4, kB, kR>);
+    default: return nullptr;
+    }
+}
+
+template <bool kB>
+const void *row_kernel_b(int n, int ppt, bool residual)
+{
+    if (!residual)
+        return n == 1 ? row_kernel_np<1, kB, false>(ppt) : nullptr;
+    switch (n) {
+    case 1: return row_kernel_np<1, kB, true>(ppt);
+    case 2: return row_kernel_np<2, kB, true>(ppt);
+    case 3: return row_kernel_np<3, kB, true>(ppt);
+    case 4: return row_kernel_np<4, kB, true>(ppt);
+    case 5: return row_kernel_np<5, kB, true>(ppt);
+    case 6: return row_kernel_np<6, kB, true>(ppt);
+    case 7: return row_kernel_np<7, kB, true>(ppt);
+    case 8: return row_kernel_np<8, kB, true>(ppt);
+    default: return nullptr;
+    }
+}
+
+const void *row_kernel(int n, int ppt, bool bpermute, bool residual)
+{
+    return bpermute ? row_kernel_b<true>(n, ppt, residual) : row_kernel_b<false>(n, ppt, residual);
+}
+
+const void *flat_kernel(int n)
+{
+    switch (n) {
+    case 1: return reinterpret_cast<const void *>(&fa::k_flat_reduce<1>);
+    case 2: return reinterpret_cast<const void *>(&fa::k_flat_reduce<2>);
+    case 3: return reinterpret_cast<const void *>(&fa::k_flat_reduce<3>);
+    case 4: return reinterpret_cast<const void *>(&fa::k_flat_reduce<4>);
+    case 5: return reinterpret_cast<const void *>(&fa::k_flat_reduce<5>);
+    case 6: return reinterpret_cast<const void *>(&fa::k_flat_reduce<6>);
+    case 7: return reinterpret_cast<const void *>(&fa::k_flat_reduce<7>);
+    case 8: return reinterpret_cast<const void *>(&fa::k_flat_reduce<8>);
+    default: return nullptr;
+    }
+}
+
+const void *lds_kernel(int n)
+{
+    switch (n) {
+    case 1: return reinterpret_cast<const void *>(&fa::k_stage1_lds<1>);
+    case 2: return reinterpret_cast<const void *>(&fa::k_stage1_lds<2>);
+    case 3: return reinterpret_cast<const void *>(&fa::k_stage1_lds<3>);
+    case 4: return reinterpret_cast<const void *>(&fa::k_stage1_lds<4>);
+    case 5: return reinterpret_cast<const void *>(&fa::k_stage1_lds<5>);
+    case 6: return reinterpret_cast<const void *>(&fa::k_stage1_lds<6>);
+    case 7: return reinterpret_cast<const void *>(&fa::k_stage1_lds<7>);
+    case 8: return reinterpret_cast<const void *>(&fa::k_stage1_lds<8>);
+    default: return nullptr;
+    }
+}
+
+struct Step {
+    const void *kernel;
+    const char *name;
+    unsigned grid, block, per_thread, launches;
+    int n;  // inputs this step reads
+};
+
+struct Plan {
+    int path;  // FUSED_AR_PATH_ONESTAGE, FUSED_AR_PATH_TWOSTAGE or kPathUnfusedPlan
+    int steps;
+    Step step[3];
+};
+
+Step flat_step(const void *kernel, const char *name, int n, size_t total_packs, unsigned block)
+{
+    size_t g = (total_packs + block - 1) / block;
+    if (g > kFlatMaxGrid)
+        g = kFlatMaxGrid;
+    const size_t covered = g * block;
+    return {kernel, name, static_cast<unsigned>(g), block,
+            static_cast<unsigned>((total_packs + covered - 1) / covered), 1, n};
+}
+
+// The launches of one call along `path` (one-stage, two-stage or the unfused sequence).
+int make_plan(int n, int m, int hidden, int path, const Options &o, Plan *plan)
+{
+    memset(plan, 0, sizeof(*plan));
+    plan->path = path;
+    if (m == 0)
+        return FUSED_AR_OK;
     const int packs = hidden / kPackElems;
+    int ppt, threads;
+    const int rc = row_geometry(packs, m, o.ppt, &ppt, &threads);
+    if (rc != FUSED_AR_OK)
+        return rc;
+    const size_t total = (size_t)m * (size_t)packs;
+    Step rows{nullptr, "", static_cast<unsigned>(m < kRowsPerLaunch ? m : kRowsPerLaunch),
+              static_cast<unsigned>(threads), static_cast<unsigned>(ppt),
+              static_cast<unsigned>((m + kRowsPerLaunch - 1) / kRowsPerLaunch), n};
+    if (path == FUSED_AR_PATH_ONESTAGE) {
+        rows.kernel = row_kernel(n, ppt, o.bpermute, true);
+        rows.name = "onestage";
+        plan->steps = 1;
+        plan->step[0] = rows;
+        return FUSED_AR_OK;
+    }
+    if (o.lds_stage1) {
+        const unsigned block = 64u * static_cast<unsigned>(n);
+        const size_t g = (total + block - 1) / block;
+        if (g > 0x7FFFFFFFu / block)
+            return FUSED_AR_ERR_SHAPE;  // the LDS-staged kernel does not stride
+        plan->step[0] = {lds_kernel(n), "stage1_reduce_lds", static_cast<unsigned>(g), block, 1, 1, n};
+    } else {
+        plan->step[0] = flat_step(flat_kernel(n), "stage1_reduce", n, total, o.flat_block);
+    }
+    rows.n = 1;
+    if (path == FUSED_AR_PATH_TWOSTAGE) {
+        rows.kernel = row_kernel(1, ppt, o.bpermute, true);
+        rows.name = "stage2_norm";
+        plan->steps = 2;
+        plan->step[1] = rows;
+        return FUSED_AR_OK;
+    }
+    // unfused: the residual add is the flat reduce of (reduced, residual); then a plain RMSNorm
+    plan->step[1] = flat_step(flat_kernel(2), "residual_add", 2, total, o.flat_block);
+    rows.kernel = row_kernel(1, ppt, o.bpermute, false);
+    rows.name = "rmsnorm";
+    plan->steps = 3;
+    plan->step[2] = rows;
+    return FUSED_AR_OK;
+}
+
+int launch(const void *kernel, unsigned grid, unsigned block, void *args, hipStream_t stream)
+{
+    void *params[] = {args};
+    const hipError_t e = hipLaunchKernel(kernel, dim3(grid), dim3(block), params, 0, stream);
+    return e == hipSuccess ? FUSED_AR_OK : static_cast<int>(e);
+}
+
+// One workgroup per row, at most kRowsPerLaunch rows per launch; later launches start
+// kRowsPerLaunch rows further into every [m, hidden] buffer.
+int run_rows(const Step &s, const RowArgs &args, int m, int packs, hipStream_t stream)
+{
+    for (int first = 0; first < m; first += kRowsPerLaunch) {
+        const int rows = m - first < kRowsPerLaunch ? m - first : kRowsPerLaunch;
+        const size_t skip = (size_t)first * (size_t)packs;  // in packs
+        RowArgs a = args;
+        for (int i = 0; i < s.n; ++i)
+            a.in[i] += skip;
+        a.residual += skip;
+        a.residual_out += skip;
+        a.out += skip;
+        const int rc = launch(s.kernel, static_cast<unsigned>(rows), s.block, &a, stream);
+        if (rc != FUSED_AR_OK)
+            return rc;
+    }
+    return FUSED_AR_OK;
+}
+
+int run_flat(const Step &s, const u32x4 *const *inputs, size_t total_packs, u32x4 *dst,
+             hipStream_t stream)
+{
+    FlatArgs a{};
+    for (int i = 0; i < s.n; ++i)
+        a.in[i] = inputs[i];
+    a.out = dst;
+    a.total_packs = total_packs;
+    return launch(s.kernel, s.grid, s.block, &a, stream);
+}
+
+// Runs a validated call (m > 0) along `plan`.
+int execute(const Plan &plan, const fa_bf16 *const *inputs, int n, const fa_bf16 *residual,
+            const fa_bf16 *weight, float eps, int m, int hidden, fa_bf16 *residual_out,
+            fa_bf16 *out, hipStream_t stream)
+{
+    const int packs = hidden / kPackElems;
+    const size_t total = (size_t)m * (size_t)packs;
+    const u32x4 *ins[FUSED_AR_MAX_INPUTS];
+    for (int i = 0; i < n; ++i)
+        ins[i] = reinterpret_cast<const u32x4 *>(inputs[i]);
+    u32x4 *ro = reinterpret_cast<u32x4 *>(residual_out);
+    u32x4 *o = reinterpret_cast<u32x4 *>(out);
+
     RowArgs a{};
-    a.residual = reinterpret_cast<const fa::u32x4 *>(residual);
-    a.weight = reinterpret_cast<const fa::u32x4 *>(weight);
-    a.residual_out = reinterpret_cast<fa::u32x4 *>(residual_out);
-    a.out = reinterpret_cast<fa::u32x4 *>(out);
+    a.residual = reinterpret_cast<const u32x4 *>(residual);
+    a.weight = reinterpret_cast<const u32x4 *>(weight);
+    a.residual_out = ro;
+    a.out = o;
     a.eps = eps;
     a.hidden = static_cast<float>(hidden);
     a.packs = packs;
 
-    if (path == FUSED_AR_PATH_ONESTAGE) {
+    if (plan.path == FUSED_AR_PATH_ONESTAGE) {
         for (int i = 0; i < n; ++i)
-            a.in[i] = reinterpret_cast<const fa::u32x4 *>(inputs[i]);
-        return run_rows(a, n, m, packs, stream);
+            a.in[i] = ins[i];
+        return run_rows(plan.step[0], a, m, packs, stream);
     }
-
-    // Two-stage: the flat reduce writes the reduced rows into `out`, then the row kernel with a
-    // single input reads them back from there and overwrites them with the normalised rows.
-    rc = run_flat(inputs, n, (size_t)m * (size_t)packs, out, stream);
+    // Two-stage and unfused: the reduce writes the reduced rows into `out`.
+    int rc = run_flat(plan.step[0], ins, total, o, stream);
     if (rc != FUSED_AR_OK)
         return rc;
-    a.in[0] = reinterpret_cast<const fa::u32x4 *>(out);
-    return run_rows(a, 1, m, packs, stream);
+    if (plan.path == FUSED_AR_PATH_TWOSTAGE) {
+        // the row kernel with a single input reads the reduced rows back from `out` and
+        // overwrites them with the normalised rows
+        a.in[0] = o;
+        return run_rows(plan.step[1], a, m, packs, stream);
+    }
+    // Unfused: residual_out = bf16(reduced + residual), then out = RMSNorm(residual_out).
+    const u32x4 *pair[2] = {o, reinterpret_cast<const u32x4 *>(residual)};
+    rc = run_flat(plan.step[1], pair, total, ro, stream);
+    if (rc != FUSED_AR_OK)
+        return rc;
+    a.in[0] = ro;
+    return run_rows(plan.step[2], a, m, packs, stream);
+}
+
+int resolve_path(int n, int m, int hidden, int path)
+{
+    if (path == FUSED_AR_PATH_UNFUSED)
+        return kPathUnfusedPlan;
+    return path == FUSED_AR_PATH_AUTO ? fused_ar_auto_path(n, m, hidden) : path;
+}
+
+}  // namespace
+
+extern "C" int fused_ar_auto_path(int n, int m, int hidden)
+{
+    (void)hidden;
+    if (n < 1 || n > FUSED_AR_MAX_INPUTS || m < 0)
+        return FUSED_AR_ERR_INVALID;
+    const int one_stage_max_m = n <= 4 ? 32 : 16;
+    return m <= one_stage_max_m ? FUSED_AR_PATH_ONESTAGE : FUSED_AR_PATH_TWOSTAGE;
+}
+
+extern "C" int fused_ar_rmsnorm_check(const fa_bf16 *const *inputs, int n,
+                                      const fa_bf16 *residual, const fa_bf16 *weight, float eps,
+                                      int m, int hidden, const fa_bf16 *residual_out,
+                                      const fa_bf16 *out, int path)
+{
+    const int rc = check_scalars(n, m, hidden, eps, path, true);
+    if (rc != FUSED_AR_OK || m == 0)
+        return rc;
+    return check_buffers(inputs, n, residual, weight, m, hidden, residual_out, out);
+}
+
+extern "C" int fused_ar_rmsnorm_ex(const fa_bf16 *const *inputs, int n, const fa_bf16 *residual,
+                                   const fa_bf16 *weight, float eps, int m, int hidden,
+                                   fa_bf16 *residual_out, fa_bf16 *out, int path,
+                                   const fused_ar_options *options, hipStream_t stream)
+{
+    Options o;
+    int rc = read_options(options, &o);
+    if (rc != FUSED_AR_OK)
+        return rc;
+    const bool unfused = path == FUSED_AR_PATH_UNFUSED;
+    rc = fused_ar_rmsnorm_check(inputs, n, residual, weight, eps, m, hidden, residual_out, out,
+                                unfused ? FUSED_AR_PATH_AUTO : path);
+    if (rc != FUSED_AR_OK || m == 0)
+        return rc;
+    Plan plan;
+    rc = make_plan(n, m, hidden, resolve_path(n, m, hidden, path), o, &plan);
+    if (rc != FUSED_AR_OK)
+        return rc;
+    return execute(plan, inputs, n, residual, weight, eps, m, hidden, residual_out, out, stream);
+}
+
+extern "C" int fused_ar_rmsnorm(const fa_bf16 *const *inputs, int n, const fa_bf16 *residual,
+                                const fa_bf16 *weight, float eps, int m, int hidden,
+                                fa_bf16 *residual_out, fa_bf16 *out, int path, hipStream_t stream)
+{
+    if (path == FUSED_AR_PATH_UNFUSED)
+        return FUSED_AR_ERR_INVALID;  // the unfused sequence has its own entry point
+    return fused_ar_rmsnorm_ex(inputs, n, residual, weight, eps, m, hidden, residual_out, out,
+                               path, nullptr, stream);
+}
+
+extern "C" int fused_ar_unfused_rmsnorm(const fa_bf16 *const *inputs, int n,
+                                        const fa_bf16 *residual, const fa_bf16 *weight, float eps,
+                                        int m, int hidden, fa_bf16 *residual_out, fa_bf16 *out,
+                                        hipStream_t stream)
+{
+    return fused_ar_rmsnorm_ex(inputs, n, residual, weight, eps, m, hidden, residual_out, out,
+                               FUSED_AR_PATH_UNFUSED, nullptr, stream);
 }
 
 extern "C" int fused_ar_reduce(const fa_bf16 *const *inputs, int n, int m, int hidden,
@@ -271,7 +459,7 @@ extern "C" int fused_ar_reduce(const fa_bf16 *const *inputs, int n, int m, int h
         if (inputs[i] == nullptr)
             return FUSED_AR_ERR_INVALID;
     const size_t total_packs = (size_t)m * (size_t)(hidden / kPackElems);
-    const size_t plane = total_packs * 16;
+    const size_t plane = total_packs * sizeof(u32x4);
     Span red_s, in_s[FUSED_AR_MAX_INPUTS];
     if (!make_span(reduced, plane, &red_s))
         return FUSED_AR_ERR_INVALID;
@@ -286,57 +474,56 @@ extern "C" int fused_ar_reduce(const fa_bf16 *const *inputs, int n, int m, int h
     for (int i = 0; i < n; ++i)
         if (overlaps(red_s, in_s[i]))
             return FUSED_AR_ERR_ALIAS;
-    return run_flat(inputs, n, total_packs, reduced, stream);
+    const u32x4 *ins[FUSED_AR_MAX_INPUTS];
+    for (int i = 0; i < n; ++i)
+        ins[i] = reinterpret_cast<const u32x4 *>(inputs[i]);
+    const Step s = flat_step(flat_kernel(n), "stage1_reduce", n, total_packs, kFlatBlock);
+    return run_flat(s, ins, total_packs, reinterpret_cast<u32x4 *>(reduced), stream);
+}
+
+extern "C" int fused_ar_describe_launch_ex(int n, int m, int hidden, int path,
+                                           const fused_ar_options *options,
+                                           fused_ar_launch_plan *plan)
+{
+    int rc = check_scalars(n, m, hidden, 0.0f,
+                           path == FUSED_AR_PATH_UNFUSED ? FUSED_AR_PATH_AUTO : path, true);
+    if (rc != FUSED_AR_OK)
+        return rc;
+    if (plan == nullptr)
+        return FUSED_AR_ERR_INVALID;
+    Options o;
+    rc = read_options(options, &o);
+    if (rc != FUSED_AR_OK)
+        return rc;
+    Plan p;
+    rc = make_plan(n, m, hidden, resolve_path(n, m, hidden, path), o, &p);
+    if (rc != FUSED_AR_OK)
+        return rc;
+    memset(plan, 0, sizeof(*plan));
+    plan->path = path == FUSED_AR_PATH_UNFUSED ? FUSED_AR_PATH_UNFUSED : p.path;
+    plan->kernels = p.steps;
+    for (int i = 0; i < p.steps; ++i) {
+        fused_ar_kernel_launch &k = plan->launch[i];
+        strncpy(k.name, p.step[i].name, sizeof(k.name) - 1);
+        k.grid = p.step[i].grid;
+        k.block = p.step[i].block;
+        k.per_thread = p.step[i].per_thread;
+        k.launches = p.step[i].launches;
+    }
+    return FUSED_AR_OK;
 }
 
 extern "C" int fused_ar_describe_launch(int n, int m, int hidden, int path,
                                         fused_ar_launch_plan *plan)
 {
-    const int rc = check_scalars(n, m, hidden, 0.0f, path, true);
-    if (rc != FUSED_AR_OK)
-        return rc;
-    if (plan == nullptr)
-        return FUSED_AR_ERR_INVALID;
-    memset(plan, 0, sizeof(*plan));
-    if (path == FUSED_AR_PATH_AUTO)
-        path = fused_ar_auto_path(n, m, hidden);
-    plan->path = path;
-    if (m == 0)
-        return FUSED_AR_OK;
-    const int packs = hidden / kPackElems;
-    int ppt, threads;
-    row_geometry(packs, m, &ppt, &threads);
-    fused_ar_kernel_launch rows{};
-    rows.grid = rows_grid(m);
-    rows.block = static_cast<unsigned>(threads);
-    rows.per_thread = static_cast<unsigned>(ppt);
-    rows.launches = rows_launches(m);
-    if (path == FUSED_AR_PATH_ONESTAGE) {
-        plan->kernels = 1;
-        strcpy(rows.name, "onestage");
-        plan->launch[0] = rows;
-    } else {
-        plan->kernels = 2;
-        fused_ar_kernel_launch flat{};
-        strcpy(flat.name, "stage1_reduce");
-        const size_t total = (size_t)m * (size_t)packs;
-        flat.grid = flat_grid(total);
-        flat.block = kFlatBlock;
-        const size_t covered = (size_t)flat.grid * kFlatBlock;
-        flat.per_thread = static_cast<unsigned>((total + covered - 1) / covered);
-        flat.launches = 1;
-        strcpy(rows.name, "stage2_norm");
-        plan->launch[0] = flat;
-        plan->launch[1] = rows;
-    }
-    return FUSED_AR_OK;
+    return fused_ar_describe_launch_ex(n, m, hidden, path, nullptr, plan);
 }
 
 extern "C" const char *fused_ar_strerror(int status)
 {
     switch (status) {
     case FUSED_AR_OK: return "success";
-    case FUSED_AR_ERR_INVALID: return "invalid argument (null pointer, n, m, hidden, eps or path out of range)";
+    case FUSED_AR_ERR_INVALID: return "invalid argument (null pointer, n, m, hidden, eps, path or option out of range)";
     case FUSED_AR_ERR_SHAPE: return "unsupported shape (hidden must be a multiple of 8 and at most 32768)";
     case FUSED_AR_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
     case FUSED_AR_ERR_ALIAS: return "forbidden overlap between output and other buffers";

@@ -79,9 +79,14 @@ __device__ __forceinline__ void store_stream(char *base, uint32_t off, u32x4 v)
 // writes residual_out and accumulates the square-sum, keeping only the bf16 residual_out and
 // weight packs; one workgroup reduction then gives the row statistic and the normalised row is
 // written from those registers.
-template <int N, int PPT>
+//   kBpermute  wave reduction by the ds_bpermute butterfly instead of DPP (bit-identical; for
+//              comparison with the design the pages replaced).
+//   kResidual  false: a plain RMSNorm of in[0] (N == 1), with no residual and no residual_out;
+//              the last kernel of the unfused sequence.
+template <int N, int PPT, bool kBpermute, bool kResidual>
 __global__ void __launch_bounds__(1024) k_rows(RowArgs a)
 {
+    static_assert(kResidual || N == 1, "the plain RMSNorm reads one input");
     __shared__ float slots[kMaxWaves];
     const uint32_t tid = threadIdx.x;
     const uint32_t nthreads = blockDim.x;
@@ -108,14 +113,20 @@ __global__ void __launch_bounds__(1024) k_rows(RowArgs a)
 #pragma unroll
             for (int i = 0; i < N; ++i)
                 x[i] = load_stream(in[i], off);
-            const u32x4 res = load_stream(residual, off);
+            u32x4 res;
+            if constexpr (kResidual)
+                res = load_stream(residual, off);
             w[k] = load_pack(weight, off);
             // all of this slot's loads are in flight before any arithmetic waits on one
             __builtin_amdgcn_sched_barrier(0);
-            F8 sum = widen(narrow(reduce_packs<N>(x)));  // the reduced value, in bf16
-            add_into(sum, widen(res));
-            ro[k] = narrow(sum);
-            store_stream(residual_out, off, ro[k]);
+            if constexpr (kResidual) {
+                F8 sum = widen(narrow(reduce_packs<N>(x)));  // the reduced value, in bf16
+                add_into(sum, widen(res));
+                ro[k] = narrow(sum);
+                store_stream(residual_out, off, ro[k]);
+            } else {
+                ro[k] = x[0];
+            }
             const F8 y = widen(ro[k]);
 #pragma unroll
             for (int e = 0; e < 8; ++e)
@@ -123,7 +134,7 @@ __global__ void __launch_bounds__(1024) k_rows(RowArgs a)
         }
     }
 
-    const float total = block_sum(ss, slots);
+    const float total = block_sum<kBpermute>(ss, slots);
     const float rstd = 1.0f / __builtin_sqrtf(total / a.hidden + a.eps);
 
 #pragma unroll
@@ -160,6 +171,38 @@ __global__ void __launch_bounds__(1024) k_flat_reduce(FlatArgs a)
             x[i] = load_stream(reinterpret_cast<const char *>(a.in[i]) + bytes, off);
         __builtin_amdgcn_sched_barrier(0);  // all N loads in flight before the first add
         store_stream(reinterpret_cast<char *>(a.out) + bytes, off, narrow(reduce_packs<N>(x)));
+    }
+}
+
+// Stage 1 with LDS staging, one wave per input (the "warp-per-rank" design that the flat reduce
+// replaced: aiter PR #3817, Technical Details > 2stage > reduce-scatter), kept for comparison.
+// The page describes it only as staging through LDS with a workgroup barrier, one wave per rank;
+// this is a reading of that: a workgroup of N waves owns a tile of 64 * N packs; wave w copies
+// input w's tile into LDS (N packs per lane), one barrier, then thread t reduces pack t of the
+// tile over the N staged copies in input order and stores it. Bit-identical to k_flat_reduce.
+template <int N>
+__global__ void __launch_bounds__(64 * N) k_stage1_lds(FlatArgs a)
+{
+    __shared__ u32x4 tile[N][64 * N];
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const size_t first = (size_t)blockIdx.x * (64 * N);
+    const char *src = reinterpret_cast<const char *>(a.in[wave]);
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        const int q = j * 64 + lane;
+        if (first + q < a.total_packs)
+            tile[wave][q] = load_stream(src + first * sizeof(u32x4), (uint32_t)q * sizeof(u32x4));
+    }
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (first + t < a.total_packs) {
+        u32x4 x[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            x[i] = tile[i][t];
+        store_stream(reinterpret_cast<char *>(a.out) + first * sizeof(u32x4),
+                     (uint32_t)t * sizeof(u32x4), narrow(reduce_packs<N>(x)));
     }
 }
 

@@ -33,7 +33,7 @@ __device__ __forceinline__ float lane_value(float x, int lane)
 }
 
 // Sum over the 64 lanes; the result is uniform across the wave.
-__device__ __forceinline__ float wave_sum(float x)
+__device__ __forceinline__ float wave_sum_dpp(float x)
 {
     x = x + dpp_partner<kDppQuadXor1>(x);      // pairs
     x = x + dpp_partner<kDppQuadXor2>(x);      // quads
@@ -43,12 +43,37 @@ __device__ __forceinline__ float wave_sum(float x)
     return (lane_value(x, 0) + lane_value(x, 16)) + (lane_value(x, 32) + lane_value(x, 48));
 }
 
+// The same sum by an XOR butterfly through the LDS crossbar (ds_bpermute_b32): the design the
+// DPP tree replaced (aiter PR #3817, Technical Details > 1stage), kept for comparison. Partners
+// at distance 1, 2, 4, 8 hold the same sums as the DPP steps above, and the last two steps add
+// (row 0 + row 1) + (row 2 + row 3), so both functions return bit-identical results.
+__device__ __forceinline__ float wave_sum_bpermute(float x)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int partner = __builtin_amdgcn_ds_bpermute((lane ^ d) << 2, __builtin_bit_cast(int, x));
+        x = x + __builtin_bit_cast(float, partner);
+    }
+    return lane_value(x, 0);
+}
+
+template <bool kBpermute>
+__device__ __forceinline__ float wave_sum(float x)
+{
+    if constexpr (kBpermute)
+        return wave_sum_bpermute(x);
+    else
+        return wave_sum_dpp(x);
+}
+
 // Sum over the workgroup (blockDim.x a multiple of 64, at most 1024): wave sums, one barrier,
 // then every thread adds the per-wave sums in wave order. `slots` is LDS with room for one float
 // per wave; all threads of the workgroup must call this.
+template <bool kBpermute>
 __device__ __forceinline__ float block_sum(float x, float *slots)
 {
-    const float w = wave_sum(x);
+    const float w = wave_sum<kBpermute>(x);
     const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0)
         slots[wave] = w;

@@ -9,12 +9,14 @@ buffer alternate between steps so that the working set (1.3 GB) exceeds the 256 
 Prints one JSON line: the achieved HBM bandwidth on algorithmic bytes, 2 (N + 3) m hidden +
 2 hidden per call, as `value` (GB/s), with the one-stage kernel's roofline, the per-call latency
 of the decode shapes (m = 1..32, 2000 calls captured in one HIP graph, minimum over 80 replays,
-as the aiter PR #3817 test plan times them) and the CPU oracle's rate on the same workload.
+as the aiter PR #3817 test plan times them), the unfused three-kernel baseline, the comparison of
+the kernel designs the pages replaced, and the CPU oracle's rate on the same workload.
 
     python bench.py [--steps K] [--warmup W] [--m 4096] [--path 1]
     python bench.py --copy-calib    # a plain 1 GiB device copy, for scaling HBM byte counters
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -26,6 +28,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_onestage_n8_m4096_h7168.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "all_reduce_residual_way_amd", "csrc", f)
                   for f in ("kernels.h", "bf16x8.h", "wave_sum.h", "fused_ar.hip")]
+DECODE_M = (1, 2, 4, 8, 16, 32)
 
 
 def log(msg):
@@ -45,6 +48,8 @@ def parse_args():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode latency sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the unfused baseline and the design comparison")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time spent timing the oracle")
     ap.add_argument("--copy-calib", action="store_true",
@@ -100,7 +105,85 @@ def copy_calibration(torch):
     ms = start.elapsed_time(end) / 5
     print(json.dumps({"copy_calibration": {"bytes_read": nbytes, "bytes_written": nbytes,
                                            "launches": 5, "ms_per_copy": ms,
-                                           "gbs": 2 * nbytes / ms / 1e6}}), flush=True)
+                                           "gbs": 2 * nbytes / ms / 1e9 * 1e3}}), flush=True)
+
+
+class Workload:
+    """Device buffers of one problem (optionally two copies, alternated between calls) and raw
+    calls into the library on the current stream."""
+
+    def __init__(self, torch, fa, prob, copies):
+        import numpy as np
+        self.torch, self.fa, self.lib = torch, fa, fa.library()
+        self.n, self.m, self.hidden, self.eps = prob.n, prob.m, prob.hidden, prob.eps
+
+        def to_dev(bits):
+            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+
+        base = [to_dev(x) for x in prob.inputs] + [to_dev(prob.residual)]
+        self.weight = to_dev(prob.weight)
+        self.sets = []
+        for c in range(copies):
+            t = base if c == 0 else [x.clone() for x in base]
+            self.sets.append(dict(arr=(ctypes.c_void_p * self.n)(*[x.data_ptr() for x in t[:-1]]),
+                                  keep=t, res=t[-1].data_ptr(),
+                                  ro_t=torch.empty_like(t[-1]), out_t=torch.empty_like(t[-1])))
+            self.sets[-1]["ro"] = self.sets[-1]["ro_t"].data_ptr()
+            self.sets[-1]["out"] = self.sets[-1]["out_t"].data_ptr()
+        torch.cuda.synchronize()
+
+    def call(self, i, path, options=None, stream=None):
+        s = self.sets[i % len(self.sets)]
+        h = stream if stream is not None else self.torch.cuda.current_stream().cuda_stream
+        if path == self.fa.PATH_UNFUSED and options is None:
+            rc = self.lib.fused_ar_unfused_rmsnorm(s["arr"], self.n, s["res"], self.weight.data_ptr(),
+                                                   self.eps, self.m, self.hidden, s["ro"], s["out"], h)
+        else:
+            opt = ctypes.byref(options) if options is not None else None
+            rc = self.lib.fused_ar_rmsnorm_ex(s["arr"], self.n, s["res"], self.weight.data_ptr(),
+                                              self.eps, self.m, self.hidden, s["ro"], s["out"],
+                                              path, opt, h)
+        if rc != 0:
+            raise self.fa.FusedArError(rc, "fused_ar call")
+
+    def time_ms(self, path, steps, warmup, options=None):
+        """Mean ms per call over `steps` back-to-back calls after `warmup` calls (HIP events on
+        the launch stream)."""
+        torch = self.torch
+        for i in range(warmup):
+            self.call(i, path, options)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for i in range(steps):
+            self.call(i, path, options)
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps
+
+    def graph_latency_us(self, path, options=None, calls=2000, replays=80):
+        """Per-call latency: `calls` calls captured in one HIP graph, one replay timed with
+        events, minimum over `replays` replays, divided by `calls`."""
+        torch = self.torch
+        for i in range(3):
+            self.call(0, path, options)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            h = torch.cuda.current_stream().cuda_stream
+            for _ in range(calls):
+                self.call(0, path, options, stream=h)
+        best = float("inf")
+        for _ in range(replays):
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            start.record()
+            g.replay()
+            end.record()
+            torch.cuda.synchronize()
+            best = min(best, start.elapsed_time(end))
+        del g
+        return best / calls * 1e3
 
 
 def main():
@@ -131,107 +214,78 @@ def main():
     n, m, hidden, eps, path = args.n, args.m, args.hidden, args.eps, args.path
     log(f"generating n={n} m={m} hidden={hidden}")
     prob = synth.make_problem(n, m, hidden, seed=args.seed, eps=eps, name="bandwidth")
-
-    def to_dev(bits):
-        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
-
-    sets = []
-    base = {"inputs": [to_dev(x) for x in prob.inputs], "residual": to_dev(prob.residual)}
-    weight = to_dev(prob.weight)
-    for copy in range(2):
-        s = base if copy == 0 else {"inputs": [x.clone() for x in base["inputs"]],
-                                    "residual": base["residual"].clone()}
-        s["ro"] = torch.empty_like(s["residual"])
-        s["out"] = torch.empty_like(s["residual"])
-        s["ptrs"] = [x.data_ptr() for x in s["inputs"]]
-        sets.append(s)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    handle = stream.cuda_stream
-    lib = fa.library()
-    ctypes_args = []
-    import ctypes
-    for s in sets:
-        arr = (ctypes.c_void_p * n)(*s["ptrs"])
-        ctypes_args.append(arr)
-
-    def step(i, p):
-        s = sets[i & 1]
-        rc = lib.fused_ar_rmsnorm(ctypes_args[i & 1], n, s["residual"].data_ptr(),
-                                  weight.data_ptr(), eps, m, hidden, s["ro"].data_ptr(),
-                                  s["out"].data_ptr(), p, handle)
-        if rc != 0:
-            raise fa.FusedArError(rc, "fused_ar_rmsnorm")
-
-    def timed(p, steps, warmup):
-        for i in range(warmup):
-            step(i, p)
-        torch.cuda.synchronize()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        start.record(stream)
-        for i in range(steps):
-            step(i, p)
-        end.record(stream)
-        torch.cuda.synchronize()
-        return start.elapsed_time(end) / steps
-
+    work = Workload(torch, fa, prob, copies=2)
     bytes_alg = algorithmic_bytes(n, m, hidden)
     plan = fa.describe_launch(n, m, hidden, path)
+
     log(f"timing path {path}: {args.steps} steps after {args.warmup} warm-up")
-    ms = timed(path, args.steps, args.warmup)
+    ms = work.time_ms(path, args.steps, args.warmup)
     gbs = bytes_alg / (ms * 1e-3) / 1e9
 
     # sampled parity of the timed configuration against the oracle (rows are independent)
     import oracle
     rows = np.array([0, 1, m // 2, m - 1])
-    got_ro = sets[0]["ro"][rows].cpu().view(torch.int16).numpy().view(np.uint16)
-    got_out = sets[0]["out"][rows].cpu().view(torch.int16).numpy().view(np.uint16)
+    got_ro = work.sets[0]["ro_t"][rows].cpu().view(torch.int16).numpy().view(np.uint16)
+    got_out = work.sets[0]["out_t"][rows].cpu().view(torch.int16).numpy().view(np.uint16)
     want_ro, want_out = oracle.fused([x[rows] for x in prob.inputs], prob.residual[rows],
                                      prob.weight, eps)
     ords = [np.where(b & 0x8000, -(b & 0x7FFF).astype(np.int32), b.astype(np.int32))
             for b in (got_out, want_out)]
     parity_ok = bool(np.array_equal(got_ro, want_ro) and np.abs(ords[0] - ords[1]).max() <= 1)
 
-    other = {}
+    def entry(p, pms):
+        return {"us_per_call": round(pms * 1e3, 3),
+                "gbs_algorithmic": round(bytes_alg / (pms * 1e-3) / 1e9, 1),
+                "kernels": [k["name"] for k in fa.describe_launch(n, m, hidden, p)["kernels"]]}
+
+    short = max(args.steps // 2, 10)
+    paths = {str(path): entry(path, ms)}
     for p in (1, 2):
-        pms = ms if p == path else timed(p, max(args.steps // 2, 10), args.warmup)
-        other[str(p)] = {"us_per_call": pms * 1e3,
-                         "gbs_algorithmic": bytes_alg / (pms * 1e-3) / 1e9,
-                         "kernels": [k["name"] for k in fa.describe_launch(n, m, hidden, p)["kernels"]]}
+        if str(p) not in paths:
+            paths[str(p)] = entry(p, work.time_ms(p, short, args.warmup))
+
+    extra = None
+    if not args.no_extra:
+        log("unfused baseline and design comparison")
+        ums = work.time_ms(fa.PATH_UNFUSED, short, args.warmup)
+        moved_unfused = 2 * (n + 6) * m * hidden + 2 * hidden
+        extra = {"unfused": dict(entry(fa.PATH_UNFUSED, ums),
+                                 moved_bytes=moved_unfused,
+                                 gbs_moved=round(moved_unfused / (ums * 1e-3) / 1e9, 1),
+                                 fused_speedup=round(ums / ms, 3))}
+        designs = {
+            "onestage_dpp": (1, None),
+            "onestage_bpermute": (1, fa.Options(fa.WAVE_BPERMUTE, 0, 0, 0)),
+            "twostage_flat_256": (2, None),
+            "twostage_flat_512": (2, fa.Options(0, fa.STAGE1_FLAT, 512, 0)),
+            "twostage_lds_staged": (2, fa.Options(0, fa.STAGE1_LDS, 0, 0)),
+        }
+        extra["designs_m4096_us"] = {
+            k: round(work.time_ms(p, short, args.warmup, o) * 1e3, 3) for k, (p, o) in designs.items()}
 
     decode = None
+    decode_designs = None
     if not args.no_decode:
-        decode = {}
-        dn, dh = 8, 7168
-        for dm in (1, 2, 4, 8, 16, 32):
+        decode, decode_designs = {}, {}
+        for dm in DECODE_M:
             log(f"decode latency m={dm}")
-            dp = synth.make_problem(dn, dm, dh, seed=dm, name="decode")
-            ins = [to_dev(x) for x in dp.inputs]
-            res, w = to_dev(dp.residual), to_dev(dp.weight)
-            ro, out = torch.empty_like(res), torch.empty_like(res)
-            arr = (ctypes.c_void_p * dn)(*[x.data_ptr() for x in ins])
-            for _ in range(3):
-                lib.fused_ar_rmsnorm(arr, dn, res.data_ptr(), w.data_ptr(), 1e-6, dm, dh,
-                                     ro.data_ptr(), out.data_ptr(), 1, handle)
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                gh = torch.cuda.current_stream().cuda_stream
-                for _ in range(2000):
-                    rc = lib.fused_ar_rmsnorm(arr, dn, res.data_ptr(), w.data_ptr(), 1e-6, dm, dh,
-                                              ro.data_ptr(), out.data_ptr(), 1, gh)
-                    if rc != 0:
-                        raise fa.FusedArError(rc, "fused_ar_rmsnorm (capture)")
-            best = float("inf")
-            for _ in range(80):
-                start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                start.record()
-                g.replay()
-                end.record()
-                torch.cuda.synchronize()
-                best = min(best, start.elapsed_time(end))
-            decode[str(dm)] = round(best / 2000 * 1e3, 3)  # us per call
-            del g
+            dw = Workload(torch, fa, synth.make_problem(8, dm, 7168, seed=dm, name="decode"), 1)
+            decode[str(dm)] = round(dw.graph_latency_us(1), 3)
+            if not args.no_extra and dm in (1, 32):
+                decode_designs[str(dm)] = {
+                    "onestage_dpp": decode[str(dm)],
+                    "onestage_bpermute": round(dw.graph_latency_us(
+                        1, fa.Options(fa.WAVE_BPERMUTE, 0, 0, 0)), 3),
+                    "twostage_flat_256": round(dw.graph_latency_us(2), 3),
+                    "twostage_flat_512": round(dw.graph_latency_us(
+                        2, fa.Options(0, fa.STAGE1_FLAT, 512, 0)), 3),
+                    "twostage_lds_staged": round(dw.graph_latency_us(
+                        2, fa.Options(0, fa.STAGE1_LDS, 0, 0)), 3),
+                    "unfused": round(dw.graph_latency_us(fa.PATH_UNFUSED), 3),
+                }
+            del dw
+        if args.no_extra:
+            decode_designs = None
 
     cpu = None
     if not args.no_cpu:
@@ -275,8 +329,10 @@ def main():
                      "kernel": kname, "avg_launch_us": round(ms * 1e3, 3),
                      "algorithmic_bytes_per_launch": bytes_alg},
         "cpu_baseline": cpu,
-        "paths": other,
+        "paths": paths,
         "decode_us_per_call": decode,
+        "decode_designs_us_per_call": decode_designs,
+        "extra": extra,
         "parity_sampled_rows_ok": parity_ok,
         "device": props.name,
         "cus": props.multi_processor_count,

@@ -58,7 +58,10 @@ enum {
 enum {
     FUSED_AR_PATH_AUTO = 0,     /* fused_ar_auto_path(n, m, hidden) */
     FUSED_AR_PATH_ONESTAGE = 1, /* one kernel, one row per workgroup */
-    FUSED_AR_PATH_TWOSTAGE = 2  /* flat reduce kernel, then residual + RMSNorm kernel */
+    FUSED_AR_PATH_TWOSTAGE = 2, /* flat reduce kernel, then residual + RMSNorm kernel */
+    FUSED_AR_PATH_UNFUSED = 3   /* reduce, residual add and RMSNorm as three kernels (only through
+                                   fused_ar_unfused_rmsnorm, fused_ar_rmsnorm_ex and
+                                   fused_ar_describe_launch) */
 };
 
 /*
@@ -87,6 +90,51 @@ enum {
 int fused_ar_rmsnorm(const fa_bf16 *const *inputs, int n, const fa_bf16 *residual,
                      const fa_bf16 *weight, float eps, int m, int hidden, fa_bf16 *residual_out,
                      fa_bf16 *out, int path, hipStream_t stream);
+
+/*
+ * fused_ar_unfused_rmsnorm - the same result as fused_ar_rmsnorm, bit for bit, computed the way an
+ * unfused epilogue would: an all-reduce (the flat reduce kernel) writing the reduced rows to
+ * `out`, a residual add writing residual_out, then an RMSNorm kernel reading residual_out back and
+ * writing out. The baseline that the fused paths are measured against ("the complete unfused
+ * operation" that the tokenspeed PR #968 backend falls back to: Summary (AI); the unfused baseline
+ * of its performance figures). It moves 2 (n + 6) m hidden bytes instead of 2 (n + 3) m hidden.
+ * Arguments, conventions and errors as for fused_ar_rmsnorm (no path argument).
+ */
+int fused_ar_unfused_rmsnorm(const fa_bf16 *const *inputs, int n, const fa_bf16 *residual,
+                             const fa_bf16 *weight, float eps, int m, int hidden,
+                             fa_bf16 *residual_out, fa_bf16 *out, hipStream_t stream);
+
+/* Options of fused_ar_rmsnorm_ex: alternative kernel designs, for comparison and tuning. */
+enum {
+    FUSED_AR_WAVE_DPP = 0,       /* wave reduction by a DPP butterfly (the default) */
+    FUSED_AR_WAVE_BPERMUTE = 1,  /* wave reduction by a ds_bpermute XOR butterfly: the design the
+                                    DPP tree replaced (aiter PR #3817, Technical Details > 1stage) */
+    FUSED_AR_STAGE1_FLAT = 0,    /* stage 1: one thread per pack, no LDS, no barrier (the default) */
+    FUSED_AR_STAGE1_LDS = 1      /* stage 1: one wave per input staging a tile through LDS, one
+                                    barrier: the "warp-per-rank" design the flat reduce replaced
+                                    (aiter PR #3817, Technical Details > 2stage > reduce-scatter) */
+};
+
+typedef struct {
+    int wave_reduce;       /* FUSED_AR_WAVE_DPP or FUSED_AR_WAVE_BPERMUTE */
+    int stage1;            /* FUSED_AR_STAGE1_FLAT or FUSED_AR_STAGE1_LDS */
+    int stage1_block;      /* threads per workgroup of the flat kernels: 0 = 256 (aiter PR #3817,
+                              2stage > stage-1 launch config), else a multiple of 64 in [64, 1024] */
+    int packs_per_thread;  /* row kernels: 0 = automatic, else 1, 2 or 4 (FUSED_AR_ERR_SHAPE if the
+                              row then needs more than 1024 threads) */
+} fused_ar_options;
+
+/*
+ * fused_ar_rmsnorm_ex - fused_ar_rmsnorm with `options` (NULL = the defaults, identical to
+ * fused_ar_rmsnorm); `path` may also be FUSED_AR_PATH_UNFUSED. Every option combination gives
+ * bit-identical residual_out; `out` is bit-identical too unless packs_per_thread changes the
+ * order of the row's square-sum (then within the same 1-ulp band). Bad options:
+ * FUSED_AR_ERR_INVALID. Otherwise as fused_ar_rmsnorm.
+ */
+int fused_ar_rmsnorm_ex(const fa_bf16 *const *inputs, int n, const fa_bf16 *residual,
+                        const fa_bf16 *weight, float eps, int m, int hidden, fa_bf16 *residual_out,
+                        fa_bf16 *out, int path, const fused_ar_options *options,
+                        hipStream_t stream);
 
 /*
  * fused_ar_rmsnorm_check - the argument checks of fused_ar_rmsnorm alone, with the same arguments
@@ -125,7 +173,8 @@ int fused_ar_auto_path(int n, int m, int hidden);
 
 /* One kernel launch of a call, as fused_ar_describe_launch reports it. */
 typedef struct {
-    char name[32];        /* kernel name: "onestage", "stage1_reduce" or "stage2_norm" */
+    char name[32];        /* kernel name: "onestage", "stage1_reduce", "stage1_reduce_lds",
+                             "stage2_norm", "residual_add" or "rmsnorm" */
     unsigned grid;        /* workgroups per launch (the row kernels: one per row) */
     unsigned block;       /* threads per workgroup (a multiple of 64) */
     unsigned per_thread;  /* 8-element packs each thread handles per row (or per stride) */
@@ -134,17 +183,20 @@ typedef struct {
 } fused_ar_kernel_launch;
 
 typedef struct {
-    int path;                       /* resolved path: 1 or 2 */
-    int kernels;                    /* launches per call: 1 or 2 */
-    fused_ar_kernel_launch launch[2];
+    int path;                       /* resolved path: 1, 2 or 3 (unfused) */
+    int kernels;                    /* kernels per call: 1, 2 or 3; 0 when m == 0 */
+    fused_ar_kernel_launch launch[3];
 } fused_ar_launch_plan;
 
 /*
- * fused_ar_describe_launch - the kernels, grids and workgroup sizes fused_ar_rmsnorm would use
- * for (n, m, hidden, path), without launching anything. For benchmarks and tests.
- * Returns FUSED_AR_OK, or the error fused_ar_rmsnorm would give for these scalars.
+ * fused_ar_describe_launch - the kernels, grids and workgroup sizes fused_ar_rmsnorm (or, for
+ * FUSED_AR_PATH_UNFUSED, fused_ar_unfused_rmsnorm) would use for (n, m, hidden, path), without
+ * launching anything. For benchmarks and tests. Returns FUSED_AR_OK, or the error the call would
+ * give for these scalars. fused_ar_describe_launch_ex does the same for fused_ar_rmsnorm_ex.
  */
 int fused_ar_describe_launch(int n, int m, int hidden, int path, fused_ar_launch_plan *plan);
+int fused_ar_describe_launch_ex(int n, int m, int hidden, int path,
+                                const fused_ar_options *options, fused_ar_launch_plan *plan);
 
 /* fused_ar_strerror - a static, human-readable description of a status code. Never NULL. */
 const char *fused_ar_strerror(int status);

@@ -29,8 +29,10 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    assert {"fused_ar_rmsnorm", "fused_ar_reduce", "fused_ar_auto_path",
-            "fused_ar_describe_launch", "fused_ar_strerror"} <= set(names)
+    assert {"fused_ar_rmsnorm", "fused_ar_rmsnorm_ex", "fused_ar_unfused_rmsnorm",
+            "fused_ar_rmsnorm_check", "fused_ar_reduce", "fused_ar_auto_path",
+            "fused_ar_describe_launch", "fused_ar_describe_launch_ex",
+            "fused_ar_strerror"} <= set(names)
 
 
 def test_library_exports_every_declared_function():
@@ -46,7 +48,10 @@ def test_header_constants_match_binding():
                         ("FUSED_AR_ERR_SHAPE", fa.ERR_SHAPE), ("FUSED_AR_ERR_ALIGN", fa.ERR_ALIGN),
                         ("FUSED_AR_ERR_ALIAS", fa.ERR_ALIAS), ("FUSED_AR_PATH_AUTO", fa.PATH_AUTO),
                         ("FUSED_AR_PATH_ONESTAGE", fa.PATH_ONESTAGE),
-                        ("FUSED_AR_PATH_TWOSTAGE", fa.PATH_TWOSTAGE)]:
+                        ("FUSED_AR_PATH_TWOSTAGE", fa.PATH_TWOSTAGE),
+                        ("FUSED_AR_PATH_UNFUSED", fa.PATH_UNFUSED),
+                        ("FUSED_AR_WAVE_DPP", fa.WAVE_DPP), ("FUSED_AR_WAVE_BPERMUTE", fa.WAVE_BPERMUTE),
+                        ("FUSED_AR_STAGE1_FLAT", fa.STAGE1_FLAT), ("FUSED_AR_STAGE1_LDS", fa.STAGE1_LDS)]:
         assert re.search(rf"\b{name}\s*=\s*{value}\b", text), name
     assert re.search(rf"#define FUSED_AR_MAX_INPUTS {fa.MAX_INPUTS}\b", text)
     assert re.search(rf"#define FUSED_AR_MAX_HIDDEN {fa.MAX_HIDDEN}\b", text)
@@ -163,12 +168,18 @@ def test_launch_geometry_covers_each_row(hidden):
 
 
 def test_launch_geometry_by_row_count():
-    # few rows: one pack per thread (a row in one memory round trip); many rows: two packs per
-    # thread for rows wider than 512 packs; rows come in launches of at most 2^20 workgroups
+    # one pack per thread, except two for 256 < m <= 1024 on rows wider than 512 packs; rows come
+    # in launches of at most 2^20 workgroups
     k = fa.describe_launch(8, 256, 7168, 1)["kernels"][0]
     assert (k["per_thread"], k["block"], k["launches"]) == (1, 896, 1)
     k = fa.describe_launch(8, 257, 7168, 1)["kernels"][0]
     assert (k["per_thread"], k["block"]) == (2, 448)
+    k = fa.describe_launch(8, 1024, 7168, 1)["kernels"][0]
+    assert (k["per_thread"], k["block"]) == (2, 448)
+    k = fa.describe_launch(8, 1025, 7168, 1)["kernels"][0]
+    assert (k["per_thread"], k["block"]) == (1, 896)
+    k = fa.describe_launch(8, 4096, 16384, 1)["kernels"][0]
+    assert (k["per_thread"], k["block"]) == (2, 1024)
     k = fa.describe_launch(8, 4096, 2880, 1)["kernels"][0]
     assert (k["per_thread"], k["block"]) == (1, 384)
     k = fa.describe_launch(2, (1 << 20) + 3, 8, 2)["kernels"][1]
@@ -199,3 +210,57 @@ def test_binding_rejects_bad_tensors_without_a_gpu():
         fa.fused_ar_rmsnorm([x.float()], x, torch.zeros(16, dtype=torch.bfloat16))
     with pytest.raises(ValueError):
         fa.fused_ar_rmsnorm([], x, x[0])
+
+
+def test_options_struct_matches_header():
+    with open(HEADER) as f:
+        text = f.read()
+    body = re.search(r"typedef struct \{(.*?)\} fused_ar_options;", text, re.S).group(1)
+    fields = re.findall(r"int (\w+);", body)
+    assert fields == [name for name, _ in fa.Options._fields_]
+
+
+@pytest.mark.parametrize("opts", [
+    fa.Options(2, 0, 0, 0), fa.Options(-1, 0, 0, 0), fa.Options(0, 2, 0, 0),
+    fa.Options(0, 0, 32, 0), fa.Options(0, 0, 100, 0), fa.Options(0, 0, 2048, 0),
+    fa.Options(0, 0, 0, 3), fa.Options(0, 0, 0, 8)])
+def test_bad_options_rejected_before_launch(opts):
+    ins = [addr(i) for i in range(4)]
+    rc = fa.fused_ar_rmsnorm_ex_ptrs(ins, addr(10), addr(11), 1e-6, 8, 4096, addr(12), addr(13),
+                                     1, opts, 0)
+    assert rc == fa.ERR_INVALID
+    with pytest.raises(fa.FusedArError):
+        fa.describe_launch(4, 8, 4096, 1, opts)
+
+
+def test_option_plans():
+    k = fa.describe_launch(8, 100, 7168, 2, fa.Options(0, fa.STAGE1_LDS, 0, 0))["kernels"]
+    assert k[0]["name"] == "stage1_reduce_lds" and k[0]["block"] == 512
+    assert k[0]["grid"] * 512 >= 100 * 896
+    k = fa.describe_launch(4, 100, 7168, 2, fa.Options(0, 0, 512, 0))["kernels"]
+    assert k[0]["block"] == 512 and k[0]["grid"] == (100 * 896 + 511) // 512
+    k = fa.describe_launch(8, 100, 7168, 1, fa.Options(0, 0, 0, 4))["kernels"]
+    assert (k[0]["per_thread"], k[0]["block"]) == (4, 256)
+    # a forced packs-per-thread that leaves the row needing more than 1024 threads
+    with pytest.raises(fa.FusedArError) as e:
+        fa.describe_launch(8, 100, 16384, 1, fa.Options(0, 0, 0, 1))
+    assert e.value.status == fa.ERR_SHAPE
+
+
+def test_unfused_plan_and_checks():
+    plan = fa.describe_launch(8, 4096, 7168, fa.PATH_UNFUSED)
+    assert plan["path"] == fa.PATH_UNFUSED
+    assert [k["name"] for k in plan["kernels"]] == ["stage1_reduce", "residual_add", "rmsnorm"]
+    # the row geometry of the RMSNorm kernel is the one-stage kernel's (identical reduction tree)
+    one = fa.describe_launch(8, 4096, 7168, 1)["kernels"][0]
+    assert (plan["kernels"][2]["block"], plan["kernels"][2]["per_thread"]) == \
+        (one["block"], one["per_thread"])
+    ins = [addr(i) for i in range(4)]
+    assert fa.fused_ar_unfused_rmsnorm_ptrs(ins, addr(10), addr(11), 1e-6, 8, 4100, addr(12),
+                                            addr(13)) == fa.ERR_SHAPE
+    assert fa.fused_ar_unfused_rmsnorm_ptrs(ins, addr(10), addr(11), 1e-6, 8, 4096, addr(12),
+                                            addr(1)) == fa.ERR_ALIAS
+    assert fa.fused_ar_unfused_rmsnorm_ptrs([0], 0, 0, 1e-6, 0, 4096, 0, 0) == fa.OK
+    # the plain entry point does not take the unfused path id
+    assert fa.fused_ar_rmsnorm_ptrs(ins, addr(10), addr(11), 1e-6, 8, 4096, addr(12), addr(13),
+                                    fa.PATH_UNFUSED, 0) == fa.ERR_INVALID

@@ -242,9 +242,9 @@ def test_large_values_and_ties():
         check_problem(p, path)
 
 
-@pytest.mark.parametrize("m", [256, 257])
+@pytest.mark.parametrize("m", [256, 257, 1024, 1025])
 def test_both_row_geometries(m):
-    """Either side of the row count where the row kernel switches from one to two packs per
+    """Either side of the row counts where the row kernel switches between one and two packs per
     thread (hidden = 7168)."""
     p = synth.make_problem(8, m, 7168, seed=16, name="geometry")
     for path in (1, 2):
@@ -318,3 +318,86 @@ def test_graph_replay_matches_eager():
         assert torch.equal(out2.view(torch.int16), out2_e.view(torch.int16)), replay
     want_ro, want_out = oracle_rows(p)
     assert_parity("graph", host(ro), host(out), want_ro, want_out)
+
+
+# ------------------------------------------------------------------------- unfused baseline
+
+@pytest.mark.parametrize("n,m,hidden", [(8, 16, 7168), (4, 300, 7168), (8, 33, 2880), (3, 5, 520),
+                                        (8, 2048, 7168)])
+def test_unfused_matches_fused_bit_for_bit(n, m, hidden):
+    """The unfused three-kernel sequence gives the fused result exactly: same reduce order, same
+    bf16 roundings, and its RMSNorm kernel has the one-stage kernel's reduction tree."""
+    p = synth.make_problem(n, m, hidden, seed=17, name="unfused")
+    ins = [dev(x) for x in p.inputs]
+    res, w = dev(p.residual), dev(p.weight)
+    announce(f"unfused n={n} m={m} hidden={hidden}")
+    ro_u, out_u = fa.fused_ar_unfused_rmsnorm(ins, res, w, p.eps)
+    ro_f, out_f = fa.fused_ar_rmsnorm(ins, res, w, p.eps, path=1)
+    torch.cuda.synchronize()
+    assert torch.equal(ro_u.view(torch.int16), ro_f.view(torch.int16))
+    assert torch.equal(out_u.view(torch.int16), out_f.view(torch.int16))
+    rows = sample_rows(p, count=16) if m > 64 else None
+    want_ro, want_out = oracle_rows(p, rows)
+    got_ro, got_out = host(ro_u), host(out_u)
+    if rows is not None:
+        got_ro, got_out = got_ro[rows], got_out[rows]
+    assert_parity("unfused", got_ro, got_out, want_ro, want_out)
+
+
+def test_unfused_in_place_residual():
+    p = synth.make_problem(8, 40, 2880, seed=18, name="unfused in place")
+    ins = [dev(x) for x in p.inputs]
+    res, w = dev(p.residual), dev(p.weight)
+    announce("unfused in place")
+    ro, out = fa.fused_ar_unfused_rmsnorm(ins, res, w, p.eps, residual_out=res)
+    torch.cuda.synchronize()
+    want_ro, want_out = oracle_rows(p)
+    assert_parity("unfused in place", host(ro), host(out), want_ro, want_out)
+
+
+# ------------------------------------------------------------------------- design options
+
+OPTION_SETS = [
+    (fa.WAVE_BPERMUTE, fa.STAGE1_FLAT, 0, 0),
+    (fa.WAVE_DPP, fa.STAGE1_LDS, 0, 0),
+    (fa.WAVE_BPERMUTE, fa.STAGE1_LDS, 512, 0),
+    (fa.WAVE_DPP, fa.STAGE1_FLAT, 512, 0),
+    (fa.WAVE_DPP, fa.STAGE1_FLAT, 64, 0),
+    (fa.WAVE_DPP, fa.STAGE1_FLAT, 1024, 0),
+]
+
+
+@pytest.mark.parametrize("opt", OPTION_SETS, ids=lambda o: "w{}-s{}-b{}-p{}".format(*o))
+@pytest.mark.parametrize("n,m,hidden", [(8, 37, 7168), (3, 11, 520), (5, 300, 2880), (1, 9, 64)])
+def test_design_options_are_bit_identical(opt, n, m, hidden):
+    """The ds_bpermute wave reduction, the LDS-staged stage 1 and other stage-1 workgroup sizes
+    give exactly the default kernels' bits on both paths (and so the oracle's)."""
+    p = synth.make_problem(n, m, hidden, seed=19, name="options")
+    ins = [dev(x) for x in p.inputs]
+    res, w = dev(p.residual), dev(p.weight)
+    announce(f"options {opt} n={n} m={m} hidden={hidden}")
+    for path in (1, 2, fa.PATH_UNFUSED):
+        ro_d, out_d = fa.fused_ar_rmsnorm(ins, res, w, p.eps, path=path)
+        ro_o, out_o = fa.fused_ar_rmsnorm(ins, res, w, p.eps, path=path, options=fa.Options(*opt))
+        torch.cuda.synchronize()
+        assert torch.equal(ro_o.view(torch.int16), ro_d.view(torch.int16)), path
+        assert torch.equal(out_o.view(torch.int16), out_d.view(torch.int16)), path
+    want_ro, want_out = oracle_rows(p)
+    assert_parity("options", host(ro_o), host(out_o), want_ro, want_out)
+
+
+@pytest.mark.parametrize("ppt", [1, 2, 4])
+def test_forced_packs_per_thread(ppt):
+    """Every row geometry is within the oracle's bar (out may move within its 1-ulp band)."""
+    for n, m, hidden in [(8, 20, 7168), (4, 7, 2880), (2, 3, 8200)]:
+        if (hidden // 8 + ppt - 1) // ppt > 1024:
+            continue
+        p = synth.make_problem(n, m, hidden, seed=20 + ppt, name="ppt")
+        announce(f"ppt={ppt} n={n} m={m} hidden={hidden}")
+        for path in (1, 2):
+            ins = [dev(x) for x in p.inputs]
+            ro, out = fa.fused_ar_rmsnorm(ins, dev(p.residual), dev(p.weight), p.eps, path=path,
+                                          options=fa.Options(0, 0, 0, ppt))
+            torch.cuda.synchronize()
+            want_ro, want_out = oracle_rows(p)
+            assert_parity(f"ppt={ppt}", host(ro), host(out), want_ro, want_out)
