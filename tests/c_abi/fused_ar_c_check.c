@@ -1,0 +1,163 @@
+/*
+ * A C11 client of libfused_ar.so that uses nothing but include/fused_ar.h (and the HIP runtime for
+ * device memory): evidence that the boundary is a plain C ABI.
+ *
+ *   fused_ar_c_check cpu   entry points that need no GPU: path rule, launch plans, argument checks
+ *   fused_ar_c_check gpu   a ragged problem through path 1, path 2 and the unfused sequence,
+ *                          compared with the CPU oracle (liboracle.so, test infrastructure)
+ * Exit status 0 on success; the first failure is printed.
+ */
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "fused_ar.h"
+
+/* The oracle library's entry point (oracle/fused_ar_oracle.c); it has no header of its own. */
+int oracle_fused_ar_rmsnorm(const uint16_t *const *inputs, int n, const uint16_t *residual,
+                            const uint16_t *weight, float eps, int m, int hidden,
+                            uint16_t *residual_out, uint16_t *out);
+
+#define CHECK(cond)                                                                  \
+    do {                                                                             \
+        if (!(cond)) {                                                               \
+            fprintf(stderr, "%s:%d: check failed: %s\n", __FILE__, __LINE__, #cond); \
+            return 1;                                                                \
+        }                                                                            \
+    } while (0)
+
+static const fa_bf16 *fake(uintptr_t i) { return (const fa_bf16 *)(0x7F0000000000u + i * (1u << 30)); }
+
+static int cpu_checks(void)
+{
+    CHECK(fused_ar_auto_path(8, 16, 7168) == FUSED_AR_PATH_ONESTAGE);
+    CHECK(fused_ar_auto_path(8, 17, 7168) == FUSED_AR_PATH_TWOSTAGE);
+    CHECK(fused_ar_auto_path(4, 32, 7168) == FUSED_AR_PATH_ONESTAGE);
+    CHECK(fused_ar_auto_path(0, 1, 7168) == FUSED_AR_ERR_INVALID);
+
+    fused_ar_launch_plan plan;
+    CHECK(fused_ar_describe_launch(8, 4096, 7168, FUSED_AR_PATH_ONESTAGE, &plan) == FUSED_AR_OK);
+    CHECK(plan.kernels == 1 && strcmp(plan.launch[0].name, "onestage") == 0);
+    CHECK(plan.launch[0].grid == 4096 && plan.launch[0].block == 896);
+    CHECK(fused_ar_describe_launch(8, 4096, 7168, FUSED_AR_PATH_UNFUSED, &plan) == FUSED_AR_OK);
+    CHECK(plan.kernels == 3 && strcmp(plan.launch[2].name, "rmsnorm") == 0);
+    fused_ar_options opt = {FUSED_AR_WAVE_BPERMUTE, FUSED_AR_STAGE1_LDS, 0, 0};
+    CHECK(fused_ar_describe_launch_ex(4, 64, 7168, FUSED_AR_PATH_TWOSTAGE, &opt, &plan) == FUSED_AR_OK);
+    CHECK(strcmp(plan.launch[0].name, "stage1_reduce_lds") == 0 && plan.launch[0].block == 256);
+
+    const fa_bf16 *ins[3] = {fake(0), fake(1), fake(2)};
+    CHECK(fused_ar_rmsnorm_check(ins, 3, fake(3), fake(4), 1e-6f, 8, 4096, (fa_bf16 *)fake(5),
+                                 (fa_bf16 *)fake(6), FUSED_AR_PATH_AUTO) == FUSED_AR_OK);
+    CHECK(fused_ar_rmsnorm_check(ins, 3, fake(3), fake(4), 1e-6f, 8, 4100, (fa_bf16 *)fake(5),
+                                 (fa_bf16 *)fake(6), FUSED_AR_PATH_AUTO) == FUSED_AR_ERR_SHAPE);
+    CHECK(fused_ar_rmsnorm_check(ins, 3, fake(3), fake(4), 1e-6f, 8, 4096, (fa_bf16 *)fake(1),
+                                 (fa_bf16 *)fake(6), FUSED_AR_PATH_AUTO) == FUSED_AR_ERR_ALIAS);
+    CHECK(fused_ar_rmsnorm(ins, 3, fake(3), fake(4), -1.0f, 8, 4096, (fa_bf16 *)fake(5),
+                           (fa_bf16 *)fake(6), FUSED_AR_PATH_AUTO, NULL) == FUSED_AR_ERR_INVALID);
+    CHECK(fused_ar_strerror(FUSED_AR_ERR_ALIGN) != NULL);
+    printf("cpu checks passed\n");
+    return 0;
+}
+
+/* Random bf16 bits with a moderate exponent range, from a 64-bit LCG (test input only). */
+static uint64_t lcg_state = 0x853c49e6748fea9bu;
+static fa_bf16 random_bf16(int lo_exp, int hi_exp)
+{
+    lcg_state = lcg_state * 6364136223846793005u + 1442695040888963407u;
+    uint32_t r = (uint32_t)(lcg_state >> 33);
+    uint32_t sign = r & 1u, mant = (r >> 1) & 0x7Fu;
+    uint32_t expo = (uint32_t)(lo_exp + 127) + (r >> 8) % (uint32_t)(hi_exp - lo_exp + 1);
+    return (fa_bf16)((sign << 15) | (expo << 7) | mant);
+}
+
+static int ordinal(fa_bf16 b) { return (b & 0x8000) ? -(int)(b & 0x7FFF) : (int)b; }
+
+#define HIP_OK(call) CHECK((call) == hipSuccess)
+
+static int gpu_checks(void)
+{
+    enum { N = 5, M = 7, H = 520 };  /* 65 packs per row: a ragged second wave */
+    const size_t plane = (size_t)M * H;
+    fa_bf16 *h_in[N], *h_res = malloc(plane * 2), *h_w = malloc(H * 2);
+    fa_bf16 *want_ro = malloc(plane * 2), *want_out = malloc(plane * 2);
+    fa_bf16 *got_ro = malloc(plane * 2), *got_out = malloc(plane * 2);
+    CHECK(h_res && h_w && want_ro && want_out && got_ro && got_out);
+    for (int i = 0; i < N; ++i) {
+        h_in[i] = malloc(plane * 2);
+        CHECK(h_in[i]);
+        for (size_t j = 0; j < plane; ++j)
+            h_in[i][j] = random_bf16(-8, 2);
+    }
+    for (size_t j = 0; j < plane; ++j)
+        h_res[j] = random_bf16(-4, 1);
+    for (int j = 0; j < H; ++j)
+        h_w[j] = random_bf16(-1, 0);
+    const float eps = 1e-6f;
+    CHECK(oracle_fused_ar_rmsnorm((const uint16_t *const *)h_in, N, h_res, h_w, eps, M, H, want_ro,
+                                  want_out) == 0);
+
+    void *d_in[N], *d_res, *d_w, *d_ro, *d_out;
+    for (int i = 0; i < N; ++i) {
+        HIP_OK(hipMalloc(&d_in[i], plane * 2));
+        HIP_OK(hipMemcpy(d_in[i], h_in[i], plane * 2, hipMemcpyHostToDevice));
+    }
+    HIP_OK(hipMalloc(&d_res, plane * 2));
+    HIP_OK(hipMalloc(&d_w, H * 2));
+    HIP_OK(hipMalloc(&d_ro, plane * 2));
+    HIP_OK(hipMalloc(&d_out, plane * 2));
+    HIP_OK(hipMemcpy(d_res, h_res, plane * 2, hipMemcpyHostToDevice));
+    HIP_OK(hipMemcpy(d_w, h_w, H * 2, hipMemcpyHostToDevice));
+
+    const fa_bf16 *ins[N];
+    for (int i = 0; i < N; ++i)
+        ins[i] = (const fa_bf16 *)d_in[i];
+    for (int variant = 0; variant < 3; ++variant) {
+        HIP_OK(hipMemset(d_ro, 0xFF, plane * 2));
+        HIP_OK(hipMemset(d_out, 0xFF, plane * 2));
+        HIP_OK(hipDeviceSynchronize());
+        int rc;
+        if (variant < 2)
+            rc = fused_ar_rmsnorm(ins, N, d_res, d_w, eps, M, H, d_ro, d_out, variant + 1, NULL);
+        else
+            rc = fused_ar_unfused_rmsnorm(ins, N, d_res, d_w, eps, M, H, d_ro, d_out, NULL);
+        CHECK(rc == FUSED_AR_OK);
+        HIP_OK(hipDeviceSynchronize());
+        HIP_OK(hipMemcpy(got_ro, d_ro, plane * 2, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(got_out, d_out, plane * 2, hipMemcpyDeviceToHost));
+        for (size_t j = 0; j < plane; ++j) {
+            if (got_ro[j] != want_ro[j]) {
+                fprintf(stderr, "variant %d: residual_out[%zu] = %#06x, oracle %#06x\n", variant, j,
+                        got_ro[j], want_ro[j]);
+                return 1;
+            }
+            const int d = ordinal(got_out[j]) - ordinal(want_out[j]);
+            if (d > 1 || d < -1) {
+                fprintf(stderr, "variant %d: out[%zu] = %#06x, oracle %#06x\n", variant, j,
+                        got_out[j], want_out[j]);
+                return 1;
+            }
+        }
+    }
+    for (int i = 0; i < N; ++i) {
+        HIP_OK(hipFree(d_in[i]));
+        free(h_in[i]);
+    }
+    HIP_OK(hipFree(d_res));
+    HIP_OK(hipFree(d_w));
+    HIP_OK(hipFree(d_ro));
+    HIP_OK(hipFree(d_out));
+    free(h_res); free(h_w); free(want_ro); free(want_out); free(got_ro); free(got_out);
+    printf("gpu checks passed: path 1, path 2 and unfused match the oracle\n");
+    return 0;
+}
+
+int main(int argc, char **argv)
+{
+    if (argc == 2 && strcmp(argv[1], "cpu") == 0)
+        return cpu_checks();
+    if (argc == 2 && strcmp(argv[1], "gpu") == 0)
+        return gpu_checks();
+    fprintf(stderr, "usage: %s cpu|gpu\n", argv[0]);
+    return 2;
+}

@@ -1,0 +1,28 @@
+"""bench.py's host-side pieces: byte accounting, the counter-summary guard, the one-GPU rule."""
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_algorithmic_bytes():
+    # n inputs + residual read, residual_out + out written, weight read once
+    assert bench.algorithmic_bytes(8, 4096, 7168) == 2 * 11 * 4096 * 7168 + 2 * 7168 == 645937152
+    assert bench.algorithmic_bytes(4, 8, 4096) == 466944
+
+
+def test_traffic_reported_only_for_the_profiled_sources(monkeypatch):
+    t = bench.measured_traffic()
+    if t is not None:  # the committed summary matches the current kernel sources
+        assert abs(t / bench.algorithmic_bytes(8, 4096, 7168) - 1) < 0.01
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda: "0" * 64)
+    assert bench.measured_traffic() is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2 and "single MI355X" in r.stderr

@@ -235,6 +235,14 @@ def test_zero_rows_and_eps():
         assert np.array_equal(out[13], p.weight & np.uint16(0x8000))
 
 
+@pytest.mark.parametrize("eps", [0.0, 1e-2, 1.0, 100.0])
+def test_eps_values(eps):
+    """eps from 0 (no zero rows here) to far above the mean square."""
+    p = synth.make_problem(8, 9, 2880, seed=21, eps=eps, name=f"eps={eps}")
+    for path in (1, 2):
+        check_problem(p, path)
+
+
 def test_large_values_and_ties():
     """The stress mix: +-3e4 rows, whose sums land on bf16 rounding ties."""
     p = synth.make_problem(8, 300, 2880, seed=11, dist="stress", name="stress ties")
