@@ -186,6 +186,55 @@ class Workload:
         return best / calls * 1e3
 
 
+def parity_rows(m):
+    """Rows sampled for the bench's parity check: first, second, middle and last, each in
+    [0, m) and listed once."""
+    import numpy as np
+    rows = np.unique(np.clip(np.array([0, 1, m // 2, m - 1]), 0, m - 1))
+    assert rows.min() >= 0 and rows.max() < m
+    return rows
+
+
+def per_rank_share(torch, fa, work, steps, warmup):
+    """One rank's share of the two-stage path in an N-way tensor-parallel group, on local HBM:
+    stage 1 reduces only this rank's 1/N slice of the packs (here the first m/N rows), stage 2
+    normalises full rows. Stage 2 is timed as the row kernel with a single input (the kernel the
+    two-stage path runs second), reading a buffer of reduced rows."""
+    n, m, hidden = work.n, work.m, work.hidden
+    lib, h = work.lib, torch.cuda.current_stream().cuda_stream
+    s0, s1 = work.sets[0], work.sets[1 % len(work.sets)]
+    slice_m = max(m // n, 1)
+
+    def stage1(_):
+        rc = lib.fused_ar_reduce(s0["arr"], n, slice_m, hidden, s0["out"], h)
+        if rc != 0:
+            raise fa.FusedArError(rc, "fused_ar_reduce")
+
+    one = (ctypes.c_void_p * 1)(s1["out"])
+
+    def stage2(_):
+        rc = lib.fused_ar_rmsnorm_ex(one, 1, s0["res"], work.weight.data_ptr(), work.eps, m,
+                                     hidden, s0["ro"], s0["out"], 1, None, h)
+        if rc != 0:
+            raise fa.FusedArError(rc, "row kernel")
+
+    def timed(fn):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(steps):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps * 1e3
+
+    t1, t2 = timed(stage1), timed(stage2)
+    return {"rows_in_slice": slice_m, "stage1_slice_us": round(t1, 3), "stage2_us": round(t2, 3),
+            "twostage_share_us": round(t1 + t2, 3)}
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -224,9 +273,14 @@ def main():
 
     # sampled parity of the timed configuration against the oracle (rows are independent)
     import oracle
-    rows = np.array([0, 1, m // 2, m - 1])
-    got_ro = work.sets[0]["ro_t"][rows].cpu().view(torch.int16).numpy().view(np.uint16)
-    got_out = work.sets[0]["out_t"][rows].cpu().view(torch.int16).numpy().view(np.uint16)
+    rows = parity_rows(m)
+
+    def host_rows(t):  # row slices are bounds-checked on the host; no device-side gather
+        return torch.cat([t[r:r + 1] for r in rows.tolist()]).cpu().view(torch.int16).numpy() \
+            .view(np.uint16)
+
+    got_ro = host_rows(work.sets[0]["ro_t"])
+    got_out = host_rows(work.sets[0]["out_t"])
     want_ro, want_out = oracle.fused([x[rows] for x in prob.inputs], prob.residual[rows],
                                      prob.weight, eps)
     ords = [np.where(b & 0x8000, -(b & 0x7FFF).astype(np.int32), b.astype(np.int32))
@@ -260,8 +314,10 @@ def main():
             "twostage_flat_512": (2, fa.Options(0, fa.STAGE1_FLAT, 512, 0)),
             "twostage_lds_staged": (2, fa.Options(0, fa.STAGE1_LDS, 0, 0)),
         }
-        extra["designs_m4096_us"] = {
+        extra["designs_us"] = {
             k: round(work.time_ms(p, short, args.warmup, o) * 1e3, 3) for k, (p, o) in designs.items()}
+        extra["per_rank_share"] = per_rank_share(torch, fa, work, short, args.warmup)
+        extra["per_rank_share"]["onestage_us"] = round(ms * 1e3, 3)
 
     decode = None
     decode_designs = None

@@ -26,3 +26,11 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=60)
     assert r.returncode == 2 and "single MI355X" in r.stderr
+
+
+def test_parity_rows_stay_in_range():
+    # m = 1 once sampled row 1 of a one-row tensor (an out-of-bounds device gather)
+    for m in (1, 2, 3, 4096):
+        rows = bench.parity_rows(m)
+        assert rows.min() == 0 and rows.max() == m - 1 and len(set(rows.tolist())) == len(rows)
+    assert bench.parity_rows(1).tolist() == [0]
