@@ -256,9 +256,10 @@ int make_plan(int n, int m, int hidden, int path, const Options &o, Plan *plan)
     if (rc != FUSED_AR_OK)
         return rc;
     const size_t total = (size_t)m * (size_t)packs;
+    const int64_t launches = ((int64_t)m + kRowsPerLaunch - 1) / kRowsPerLaunch;
     Step rows{nullptr, "", static_cast<unsigned>(m < kRowsPerLaunch ? m : kRowsPerLaunch),
               static_cast<unsigned>(threads), static_cast<unsigned>(ppt),
-              static_cast<unsigned>((m + kRowsPerLaunch - 1) / kRowsPerLaunch), n};
+              static_cast<unsigned>(launches), n};
     if (path == FUSED_AR_PATH_ONESTAGE) {
         rows.kernel = row_kernel(n, ppt, o.bpermute, true);
         rows.name = "onestage";
@@ -303,8 +304,8 @@ int launch(const void *kernel, unsigned grid, unsigned block, void *args, hipStr
 // kRowsPerLaunch rows further into every [m, hidden] buffer.
 int run_rows(const Step &s, const RowArgs &args, int m, int packs, hipStream_t stream)
 {
-    for (int first = 0; first < m; first += kRowsPerLaunch) {
-        const int rows = m - first < kRowsPerLaunch ? m - first : kRowsPerLaunch;
+    for (int64_t first = 0; first < m; first += kRowsPerLaunch) {
+        const int rows = static_cast<int>(m - first < kRowsPerLaunch ? m - first : kRowsPerLaunch);
         const size_t skip = (size_t)first * (size_t)packs;  // in packs
         RowArgs a = args;
         for (int i = 0; i < s.n; ++i)

@@ -56,6 +56,43 @@ static int cpu_checks(void)
     CHECK(fused_ar_rmsnorm(ins, 3, fake(3), fake(4), -1.0f, 8, 4096, (fa_bf16 *)fake(5),
                            (fa_bf16 *)fake(6), FUSED_AR_PATH_AUTO, NULL) == FUSED_AR_ERR_INVALID);
     CHECK(fused_ar_strerror(FUSED_AR_ERR_ALIGN) != NULL);
+    CHECK(fused_ar_strerror(12345) != NULL && fused_ar_strerror(-12345) != NULL);
+
+    /* extremes of the scalar arguments: no overflow in the plan arithmetic */
+    CHECK(fused_ar_describe_launch(8, 2147483647, 32768, FUSED_AR_PATH_ONESTAGE, &plan) == FUSED_AR_OK);
+    CHECK(plan.launch[0].launches == 2048u && plan.launch[0].grid == (1u << 20));
+    CHECK(fused_ar_describe_launch(8, 2147483647, 32768, FUSED_AR_PATH_UNFUSED, &plan) == FUSED_AR_OK);
+    CHECK(plan.kernels == 3);
+    CHECK(fused_ar_describe_launch(8, 2147483647, 32768, FUSED_AR_PATH_TWOSTAGE, &plan) == FUSED_AR_OK);
+    fused_ar_options lds = {FUSED_AR_WAVE_DPP, FUSED_AR_STAGE1_LDS, 0, 0};
+    CHECK(fused_ar_describe_launch_ex(8, 2147483647, 32768, FUSED_AR_PATH_TWOSTAGE, &lds, &plan) ==
+          FUSED_AR_ERR_SHAPE);
+    CHECK(fused_ar_describe_launch(8, -2147483647 - 1, 8, 1, &plan) == FUSED_AR_ERR_INVALID);
+    CHECK(fused_ar_describe_launch(8, 1, 2147483647, 1, &plan) == FUSED_AR_ERR_SHAPE);
+    CHECK(fused_ar_describe_launch(8, 1, 2147483640, 1, &plan) == FUSED_AR_ERR_SHAPE);
+    CHECK(fused_ar_describe_launch(8, 1, 8, 1, NULL) == FUSED_AR_ERR_INVALID);
+    for (int n = -1; n <= 9; ++n)
+        for (int path = -1; path <= 4; ++path)
+            for (int m = 0; m <= 40; m += 17) {
+                const int rc = fused_ar_describe_launch(n, m, 7168, path, &plan);
+                CHECK(rc == ((n >= 1 && n <= 8 && path >= 0 && path <= 3) ? FUSED_AR_OK
+                                                                          : FUSED_AR_ERR_INVALID));
+            }
+    /* a huge m: the byte extents are checked without wrapping */
+    CHECK(fused_ar_rmsnorm_check(ins, 3, fake(3), fake(4), 1e-6f, 2147483647, 32768,
+                                 (fa_bf16 *)fake(5), (fa_bf16 *)fake(6), 1) == FUSED_AR_ERR_ALIAS);
+    const fa_bf16 *top[1] = {(const fa_bf16 *)(uintptr_t)0xFFFFFFFFFFFF0000u};
+    CHECK(fused_ar_rmsnorm_check(top, 1, fake(3), fake(4), 1e-6f, 8, 4096, (fa_bf16 *)fake(5),
+                                 (fa_bf16 *)fake(6), 1) == FUSED_AR_ERR_INVALID);
+    /* 2^31 rows of 2^31 - 8 elements: 2^63 bytes per plane, no size_t overflow; the extents
+       overlap the inputs, and an output near the top of the address space wraps */
+    CHECK(fused_ar_reduce(ins, 3, 2147483647, 2147483640, (fa_bf16 *)fake(9), NULL) ==
+          FUSED_AR_ERR_ALIAS);
+    CHECK(fused_ar_reduce(ins, 3, 2147483647, 2147483640,
+                          (fa_bf16 *)(uintptr_t)0xFFFF000000000000u, NULL) == FUSED_AR_ERR_INVALID);
+    fused_ar_options bad = {0, 0, 96, 0};
+    CHECK(fused_ar_rmsnorm_ex(ins, 3, fake(3), fake(4), 1e-6f, 8, 4096, (fa_bf16 *)fake(5),
+                              (fa_bf16 *)fake(6), 1, &bad, NULL) == FUSED_AR_ERR_INVALID);
     printf("cpu checks passed\n");
     return 0;
 }

@@ -409,3 +409,35 @@ def test_forced_packs_per_thread(ppt):
             torch.cuda.synchronize()
             want_ro, want_out = oracle_rows(p)
             assert_parity(f"ppt={ppt}", host(ro), host(out), want_ro, want_out)
+
+
+# ------------------------------------------------------------------------- randomized sweep
+
+def test_randomized_shapes_paths_and_options():
+    """40 seeded random cases: n in 1..8, m in 1..300, hidden any multiple of 8 up to 9600, every
+    path (auto, one-stage, two-stage, unfused), random design options and eps, normal or stress
+    values; each compared whole with the oracle."""
+    rng = np.random.default_rng(2024)
+    for case in range(40):
+        n = int(rng.integers(1, 9))
+        m = int(rng.integers(1, 301))
+        hidden = 8 * int(rng.integers(1, 1201))
+        path = int(rng.choice([0, 1, 2, fa.PATH_UNFUSED]))
+        ppt = int(rng.choice([0, 1, 2, 4]))
+        if (hidden // 8 + max(ppt, 1) - 1) // max(ppt, 1) > 1024:
+            ppt = 0
+        opt = fa.Options(int(rng.integers(0, 2)), int(rng.integers(0, 2)),
+                         int(rng.choice([0, 64, 256, 512, 1024])), ppt)
+        eps = float(rng.choice([1e-6, 1e-5, 0.1]))
+        dist = "stress" if rng.random() < 0.3 else "normal"
+        p = synth.make_problem(n, m, hidden, seed=5000 + case, eps=eps, dist=dist, name="random")
+        name = (f"random case {case}: n={n} m={m} hidden={hidden} path={path} "
+                f"options=({opt.wave_reduce},{opt.stage1},{opt.stage1_block},{opt.packs_per_thread}) "
+                f"eps={eps} {dist}")
+        announce(name)
+        ins = [dev(x) for x in p.inputs]
+        ro, out = fa.fused_ar_rmsnorm(ins, dev(p.residual), dev(p.weight), eps, path=path,
+                                      options=opt)
+        torch.cuda.synchronize()
+        want_ro, want_out = oracle_rows(p)
+        assert_parity(name, host(ro), host(out), want_ro, want_out)
