@@ -54,6 +54,9 @@ def parse_args():
                     help="minimum CPU time spent timing the oracle")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
+    ap.add_argument("--all-workloads", action="store_true",
+                    help="only measure every workload of the decode/prefill set on each of its "
+                         "paths: one JSON line per (workload, m, path)")
     return ap.parse_args()
 
 
@@ -235,6 +238,43 @@ def per_rank_share(torch, fa, work, steps, warmup):
             "twostage_share_us": round(t1 + t2, 3)}
 
 
+def all_workloads(torch, fa, synth):
+    """Each workload on its own path(s) and on paths 1 and 2. Problems whose buffers fit in the
+    256 MB Infinity Cache are timed as the pages time decode: one warm buffer set, calls captured in
+    one HIP graph (2000, fewer for long calls), min over 20 replays, per call. Larger ones run
+    back-to-back calls rotating enough buffer sets to exceed 1 GiB, so that HBM serves them."""
+    for wname, w in synth.WORKLOADS.items():
+        ms = w["ms"] if w["ms"] is not None else synth.stress_m_values(0)
+        paths = sorted(set(w["paths"]) | {1, 2})
+        for m in ms:
+            n, hidden = w["n"], w["hidden"]
+            prob = synth.make_problem(n, m, hidden, seed=1000 + m, eps=w["eps"], dist=w["dist"],
+                                      name=wname)
+            footprint = 2 * (n + 3) * m * hidden
+            warm = footprint <= (128 << 20)
+            copies = 1 if warm else min(8, max(1, -(-(1 << 30) // footprint)))
+            work = Workload(torch, fa, prob, copies)
+            bytes_alg = algorithmic_bytes(n, m, hidden)
+            for p in paths:
+                if warm:
+                    est_us = 4.0 + bytes_alg / 5e3  # rough per-call time, to size the graph
+                    calls = int(max(50, min(2000, 40e3 / est_us)))
+                    us = work.graph_latency_us(p, calls=calls, replays=20)
+                    how = f"warm, graph of {calls} calls, min of 20 replays"
+                else:
+                    steps = 100
+                    us = work.time_ms(p, steps, 10) * 1e3
+                    how = f"{steps} calls over {copies} buffer sets ({copies * footprint >> 20} MiB)"
+                gbs = bytes_alg / (us * 1e-6) / 1e9
+                print(json.dumps({"workload": wname, "n": n, "m": m, "hidden": hidden,
+                                  "eps": w["eps"], "dist": w["dist"], "path": p,
+                                  "resolved_path": fa.describe_launch(n, m, hidden, p)["path"],
+                                  "us_per_call": round(us, 3), "gbs_algorithmic": round(gbs, 1),
+                                  "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                                  "timing": how}), flush=True)
+            del work
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -258,6 +298,9 @@ def main():
 
     if args.copy_calib:
         copy_calibration(torch)
+        return
+    if args.all_workloads:
+        all_workloads(torch, fa, synth)
         return
 
     n, m, hidden, eps, path = args.n, args.m, args.hidden, args.eps, args.path
