@@ -18,7 +18,8 @@ __all__ = [
     "auto_path", "describe_launch", "strerror",
     "OK", "ERR_INVALID", "ERR_SHAPE", "ERR_ALIGN", "ERR_ALIAS",
     "PATH_AUTO", "PATH_ONESTAGE", "PATH_TWOSTAGE", "PATH_UNFUSED", "WAVE_DPP", "WAVE_BPERMUTE",
-    "STAGE1_FLAT", "STAGE1_LDS", "MAX_INPUTS", "MAX_HIDDEN",
+    "STAGE1_FLAT", "STAGE1_LDS", "LOAD_AUTO", "LOAD_CACHED", "LOAD_STREAM", "MAX_INPUTS",
+    "MAX_HIDDEN",
 ]
 
 LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfused_ar.so")
@@ -28,6 +29,7 @@ OK, ERR_INVALID, ERR_SHAPE, ERR_ALIGN, ERR_ALIAS = 0, -1, -2, -3, -4
 PATH_AUTO, PATH_ONESTAGE, PATH_TWOSTAGE, PATH_UNFUSED = 0, 1, 2, 3
 WAVE_DPP, WAVE_BPERMUTE = 0, 1
 STAGE1_FLAT, STAGE1_LDS = 0, 1
+LOAD_AUTO, LOAD_CACHED, LOAD_STREAM = 0, 1, 2
 MAX_INPUTS, MAX_HIDDEN = 8, 32768
 
 _VP = ctypes.c_void_p
@@ -35,7 +37,8 @@ _VP = ctypes.c_void_p
 
 class _KernelLaunch(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 32), ("grid", ctypes.c_uint), ("block", ctypes.c_uint),
-                ("per_thread", ctypes.c_uint), ("launches", ctypes.c_uint)]
+                ("per_thread", ctypes.c_uint), ("launches", ctypes.c_uint),
+                ("streaming", ctypes.c_uint)]
 
 
 class _LaunchPlan(ctypes.Structure):
@@ -45,7 +48,8 @@ class _LaunchPlan(ctypes.Structure):
 class Options(ctypes.Structure):
     """fused_ar_options: alternative kernel designs (see include/fused_ar.h)."""
     _fields_ = [("wave_reduce", ctypes.c_int), ("stage1", ctypes.c_int),
-                ("stage1_block", ctypes.c_int), ("packs_per_thread", ctypes.c_int)]
+                ("stage1_block", ctypes.c_int), ("packs_per_thread", ctypes.c_int),
+                ("load_policy", ctypes.c_int)]
 
 
 class FusedArError(RuntimeError):
@@ -124,7 +128,7 @@ def describe_launch(n, m, hidden, path=PATH_AUTO, options=None):
         "kernels": [
             {"name": plan.launch[i].name.decode(), "grid": plan.launch[i].grid,
              "block": plan.launch[i].block, "per_thread": plan.launch[i].per_thread,
-             "launches": plan.launch[i].launches}
+             "launches": plan.launch[i].launches, "streaming": plan.launch[i].streaming}
             for i in range(plan.kernels)
         ],
     }

@@ -53,11 +53,10 @@ __device__ __forceinline__ F8 reduce_packs(const u32x4 (&x)[N])
 }
 
 // A pack at a byte offset from a wave-uniform base (the base stays in scalar registers, the
-// per-lane offset is 32 bits). load_pack is an ordinary load, for data that is reused (the
-// weight, read by every row); load_stream is a non-temporal load, for data read exactly once
-// (the partial sums and the residual), so that the stream does not displace reused lines.
-// store_stream is a non-temporal store: nothing this library writes is read back soon enough
-// to profit from staying in the caches.
+// per-lane offset is 32 bits). load_pack is an ordinary load (the weight, read by every row, and
+// inputs that may still be cached); load_stream is a non-temporal load (inputs streamed from HBM,
+// so that they do not displace reused lines). store_stream is a non-temporal store for the
+// outputs.
 __device__ __forceinline__ u32x4 load_pack(const char *base, uint32_t off)
 {
     return *reinterpret_cast<const u32x4 *>(base + off);
@@ -73,6 +72,23 @@ __device__ __forceinline__ void store_stream(char *base, uint32_t off, u32x4 v)
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(base + off));
 }
 
+__device__ __forceinline__ void store_pack(char *base, uint32_t off, u32x4 v)
+{
+    *reinterpret_cast<u32x4 *>(base + off) = v;
+}
+
+// The load of a pack that is read once: non-temporal when kStream (data arriving from HBM; the hint
+// keeps it from displacing reused lines), an ordinary load otherwise (data that may still be in
+// the L2 or the Infinity Cache, where an ordinary load finds it).
+template <bool kStream>
+__device__ __forceinline__ u32x4 load_once(const char *base, uint32_t off)
+{
+    if constexpr (kStream)
+        return load_stream(base, off);
+    else
+        return load_pack(base, off);
+}
+
 // Workgroup b handles row b (the host launches one workgroup per row, splitting very tall
 // problems into several launches); thread t handles packs t, t + blockDim.x, ..., PPT of them.
 // For each of its packs a thread loads the N inputs, the residual and the weight, reduces,
@@ -83,7 +99,8 @@ __device__ __forceinline__ void store_stream(char *base, uint32_t off, u32x4 v)
 //              comparison with the design the pages replaced).
 //   kResidual  false: a plain RMSNorm of in[0] (N == 1), with no residual and no residual_out;
 //              the last kernel of the unfused sequence.
-template <int N, int PPT, bool kBpermute, bool kResidual>
+//   kStream    non-temporal loads of the inputs and the residual (see load_once).
+template <int N, int PPT, bool kBpermute, bool kResidual, bool kStream>
 __global__ void __launch_bounds__(1024) k_rows(RowArgs a)
 {
     static_assert(kResidual || N == 1, "the plain RMSNorm reads one input");
@@ -112,10 +129,10 @@ __global__ void __launch_bounds__(1024) k_rows(RowArgs a)
             u32x4 x[N];
 #pragma unroll
             for (int i = 0; i < N; ++i)
-                x[i] = load_stream(in[i], off);
+                x[i] = load_once<kStream>(in[i], off);
             u32x4 res;
             if constexpr (kResidual)
-                res = load_stream(residual, off);
+                res = load_once<kStream>(residual, off);
             w[k] = load_pack(weight, off);
             // all of this slot's loads are in flight before any arithmetic waits on one
             __builtin_amdgcn_sched_barrier(0);
@@ -156,7 +173,7 @@ __global__ void __launch_bounds__(1024) k_rows(RowArgs a)
 // Flat N-way reduce: workgroup b handles the blockDim.x packs starting at pack b * blockDim.x,
 // then strides by the whole grid (one pass when the grid covers the problem, which it does up to
 // 2^30 packs).
-template <int N>
+template <int N, bool kStream>
 __global__ void __launch_bounds__(1024) k_flat_reduce(FlatArgs a)
 {
     const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -168,9 +185,14 @@ __global__ void __launch_bounds__(1024) k_flat_reduce(FlatArgs a)
         u32x4 x[N];
 #pragma unroll
         for (int i = 0; i < N; ++i)
-            x[i] = load_stream(reinterpret_cast<const char *>(a.in[i]) + bytes, off);
+            x[i] = load_once<kStream>(reinterpret_cast<const char *>(a.in[i]) + bytes, off);
         __builtin_amdgcn_sched_barrier(0);  // all N loads in flight before the first add
-        store_stream(reinterpret_cast<char *>(a.out) + bytes, off, narrow(reduce_packs<N>(x)));
+        // the reduced rows are read back by the next kernel: cached unless streaming
+        const u32x4 r = narrow(reduce_packs<N>(x));
+        if constexpr (kStream)
+            store_stream(reinterpret_cast<char *>(a.out) + bytes, off, r);
+        else
+            store_pack(reinterpret_cast<char *>(a.out) + bytes, off, r);
     }
 }
 
@@ -180,7 +202,7 @@ __global__ void __launch_bounds__(1024) k_flat_reduce(FlatArgs a)
 // this is a reading of that: a workgroup of N waves owns a tile of 64 * N packs; wave w copies
 // input w's tile into LDS (N packs per lane), one barrier, then thread t reduces pack t of the
 // tile over the N staged copies in input order and stores it. Bit-identical to k_flat_reduce.
-template <int N>
+template <int N, bool kStream>
 __global__ void __launch_bounds__(64 * N) k_stage1_lds(FlatArgs a)
 {
     __shared__ u32x4 tile[N][64 * N];
@@ -192,7 +214,7 @@ __global__ void __launch_bounds__(64 * N) k_stage1_lds(FlatArgs a)
     for (int j = 0; j < N; ++j) {
         const int q = j * 64 + lane;
         if (first + q < a.total_packs)
-            tile[wave][q] = load_stream(src + first * sizeof(u32x4), (uint32_t)q * sizeof(u32x4));
+            tile[wave][q] = load_once<kStream>(src + first * sizeof(u32x4), (uint32_t)q * sizeof(u32x4));
     }
     __syncthreads();
     const int t = threadIdx.x;
@@ -201,8 +223,12 @@ __global__ void __launch_bounds__(64 * N) k_stage1_lds(FlatArgs a)
 #pragma unroll
         for (int i = 0; i < N; ++i)
             x[i] = tile[i][t];
-        store_stream(reinterpret_cast<char *>(a.out) + first * sizeof(u32x4),
-                     (uint32_t)t * sizeof(u32x4), narrow(reduce_packs<N>(x)));
+        const u32x4 r = narrow(reduce_packs<N>(x));
+        char *dst = reinterpret_cast<char *>(a.out) + first * sizeof(u32x4);
+        if constexpr (kStream)
+            store_stream(dst, (uint32_t)t * sizeof(u32x4), r);
+        else
+            store_pack(dst, (uint32_t)t * sizeof(u32x4), r);
     }
 }
 

@@ -115,6 +115,14 @@ enum {
                                     (aiter PR #3817, Technical Details > 2stage > reduce-scatter) */
 };
 
+enum {
+    FUSED_AR_LOAD_AUTO = 0,    /* ordinary loads when a call reads at most 128 MiB (its inputs may
+                                  still be in the L2s or the 256 MB Infinity Cache), non-temporal
+                                  loads above (inputs streamed from HBM) */
+    FUSED_AR_LOAD_CACHED = 1,  /* always ordinary loads */
+    FUSED_AR_LOAD_STREAM = 2   /* always non-temporal loads */
+};
+
 typedef struct {
     int wave_reduce;       /* FUSED_AR_WAVE_DPP or FUSED_AR_WAVE_BPERMUTE */
     int stage1;            /* FUSED_AR_STAGE1_FLAT or FUSED_AR_STAGE1_LDS */
@@ -122,6 +130,8 @@ typedef struct {
                               2stage > stage-1 launch config), else a multiple of 64 in [64, 1024] */
     int packs_per_thread;  /* row kernels: 0 = automatic, else 1, 2 or 4 (FUSED_AR_ERR_SHAPE if the
                               row then needs more than 1024 threads) */
+    int load_policy;       /* FUSED_AR_LOAD_AUTO, FUSED_AR_LOAD_CACHED or FUSED_AR_LOAD_STREAM: how
+                              the inputs and the residual are loaded (results are the same bits) */
 } fused_ar_options;
 
 /*
@@ -180,6 +190,7 @@ typedef struct {
     unsigned per_thread;  /* 8-element packs each thread handles per row (or per stride) */
     unsigned launches;    /* launches of this kernel per call (rows come in launches of at most
                              2^20 workgroups) */
+    unsigned streaming;   /* 1: non-temporal loads of the inputs; 0: ordinary loads */
 } fused_ar_kernel_launch;
 
 typedef struct {

@@ -42,7 +42,7 @@ static int cpu_checks(void)
     CHECK(plan.launch[0].grid == 4096 && plan.launch[0].block == 896);
     CHECK(fused_ar_describe_launch(8, 4096, 7168, FUSED_AR_PATH_UNFUSED, &plan) == FUSED_AR_OK);
     CHECK(plan.kernels == 3 && strcmp(plan.launch[2].name, "rmsnorm") == 0);
-    fused_ar_options opt = {FUSED_AR_WAVE_BPERMUTE, FUSED_AR_STAGE1_LDS, 0, 0};
+    fused_ar_options opt = {FUSED_AR_WAVE_BPERMUTE, FUSED_AR_STAGE1_LDS, 0, 0, FUSED_AR_LOAD_AUTO};
     CHECK(fused_ar_describe_launch_ex(4, 64, 7168, FUSED_AR_PATH_TWOSTAGE, &opt, &plan) == FUSED_AR_OK);
     CHECK(strcmp(plan.launch[0].name, "stage1_reduce_lds") == 0 && plan.launch[0].block == 256);
 
@@ -64,7 +64,7 @@ static int cpu_checks(void)
     CHECK(fused_ar_describe_launch(8, 2147483647, 32768, FUSED_AR_PATH_UNFUSED, &plan) == FUSED_AR_OK);
     CHECK(plan.kernels == 3);
     CHECK(fused_ar_describe_launch(8, 2147483647, 32768, FUSED_AR_PATH_TWOSTAGE, &plan) == FUSED_AR_OK);
-    fused_ar_options lds = {FUSED_AR_WAVE_DPP, FUSED_AR_STAGE1_LDS, 0, 0};
+    fused_ar_options lds = {FUSED_AR_WAVE_DPP, FUSED_AR_STAGE1_LDS, 0, 0, FUSED_AR_LOAD_STREAM};
     CHECK(fused_ar_describe_launch_ex(8, 2147483647, 32768, FUSED_AR_PATH_TWOSTAGE, &lds, &plan) ==
           FUSED_AR_ERR_SHAPE);
     CHECK(fused_ar_describe_launch(8, -2147483647 - 1, 8, 1, &plan) == FUSED_AR_ERR_INVALID);
@@ -90,9 +90,15 @@ static int cpu_checks(void)
           FUSED_AR_ERR_ALIAS);
     CHECK(fused_ar_reduce(ins, 3, 2147483647, 2147483640,
                           (fa_bf16 *)(uintptr_t)0xFFFF000000000000u, NULL) == FUSED_AR_ERR_INVALID);
-    fused_ar_options bad = {0, 0, 96, 0};
+    fused_ar_options bad = {0, 0, 96, 0, 0};
+    fused_ar_options bad_policy = {0, 0, 0, 0, 3};
     CHECK(fused_ar_rmsnorm_ex(ins, 3, fake(3), fake(4), 1e-6f, 8, 4096, (fa_bf16 *)fake(5),
                               (fa_bf16 *)fake(6), 1, &bad, NULL) == FUSED_AR_ERR_INVALID);
+    CHECK(fused_ar_rmsnorm_ex(ins, 3, fake(3), fake(4), 1e-6f, 8, 4096, (fa_bf16 *)fake(5),
+                              (fa_bf16 *)fake(6), 1, &bad_policy, NULL) == FUSED_AR_ERR_INVALID);
+    /* automatic load policy: ordinary loads up to 128 MiB read per call, streaming above */
+    CHECK(fused_ar_describe_launch(8, 1040, 7168, 1, &plan) == FUSED_AR_OK && plan.launch[0].streaming == 0);
+    CHECK(fused_ar_describe_launch(8, 1041, 7168, 1, &plan) == FUSED_AR_OK && plan.launch[0].streaming == 1);
     printf("cpu checks passed\n");
     return 0;
 }

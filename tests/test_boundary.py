@@ -51,7 +51,9 @@ def test_header_constants_match_binding():
                         ("FUSED_AR_PATH_TWOSTAGE", fa.PATH_TWOSTAGE),
                         ("FUSED_AR_PATH_UNFUSED", fa.PATH_UNFUSED),
                         ("FUSED_AR_WAVE_DPP", fa.WAVE_DPP), ("FUSED_AR_WAVE_BPERMUTE", fa.WAVE_BPERMUTE),
-                        ("FUSED_AR_STAGE1_FLAT", fa.STAGE1_FLAT), ("FUSED_AR_STAGE1_LDS", fa.STAGE1_LDS)]:
+                        ("FUSED_AR_STAGE1_FLAT", fa.STAGE1_FLAT), ("FUSED_AR_STAGE1_LDS", fa.STAGE1_LDS),
+                        ("FUSED_AR_LOAD_AUTO", fa.LOAD_AUTO), ("FUSED_AR_LOAD_CACHED", fa.LOAD_CACHED),
+                        ("FUSED_AR_LOAD_STREAM", fa.LOAD_STREAM)]:
         assert re.search(rf"\b{name}\s*=\s*{value}\b", text), name
     assert re.search(rf"#define FUSED_AR_MAX_INPUTS {fa.MAX_INPUTS}\b", text)
     assert re.search(rf"#define FUSED_AR_MAX_HIDDEN {fa.MAX_HIDDEN}\b", text)
@@ -223,7 +225,8 @@ def test_options_struct_matches_header():
 @pytest.mark.parametrize("opts", [
     fa.Options(2, 0, 0, 0), fa.Options(-1, 0, 0, 0), fa.Options(0, 2, 0, 0),
     fa.Options(0, 0, 32, 0), fa.Options(0, 0, 100, 0), fa.Options(0, 0, 2048, 0),
-    fa.Options(0, 0, 0, 3), fa.Options(0, 0, 0, 8)])
+    fa.Options(0, 0, 0, 3), fa.Options(0, 0, 0, 8), fa.Options(0, 0, 0, 0, 3),
+    fa.Options(0, 0, 0, 0, -1)])
 def test_bad_options_rejected_before_launch(opts):
     ins = [addr(i) for i in range(4)]
     rc = fa.fused_ar_rmsnorm_ex_ptrs(ins, addr(10), addr(11), 1e-6, 8, 4096, addr(12), addr(13),
@@ -264,3 +267,20 @@ def test_unfused_plan_and_checks():
     # the plain entry point does not take the unfused path id
     assert fa.fused_ar_rmsnorm_ptrs(ins, addr(10), addr(11), 1e-6, 8, 4096, addr(12), addr(13),
                                     fa.PATH_UNFUSED, 0) == fa.ERR_INVALID
+
+
+def test_automatic_load_policy():
+    """Ordinary loads while a call reads at most 128 MiB (inputs + residual), non-temporal above;
+    the same choice for every kernel of a call; forced by the option."""
+    def streaming(n, m, hidden, path=1, opt=None):
+        return [k["streaming"] for k in fa.describe_launch(n, m, hidden, path, opt)["kernels"]]
+    limit = 128 << 20
+    for n, hidden in [(8, 7168), (4, 7168), (8, 2880), (1, 8192)]:
+        per_row = 2 * (n + 1) * hidden
+        m_max = limit // per_row
+        assert streaming(n, m_max, hidden) == [0]
+        assert streaming(n, m_max + 1, hidden) == [1]
+        assert streaming(n, m_max + 1, hidden, 2) == [1, 1]
+        assert streaming(n, m_max, hidden, fa.PATH_UNFUSED) == [0, 0, 0]
+    assert streaming(8, 4096, 7168, 1, fa.Options(0, 0, 0, 0, fa.LOAD_CACHED)) == [0]
+    assert streaming(8, 8, 7168, 1, fa.Options(0, 0, 0, 0, fa.LOAD_STREAM)) == [1]

@@ -366,16 +366,17 @@ def test_unfused_in_place_residual():
 # ------------------------------------------------------------------------- design options
 
 OPTION_SETS = [
-    (fa.WAVE_BPERMUTE, fa.STAGE1_FLAT, 0, 0),
-    (fa.WAVE_DPP, fa.STAGE1_LDS, 0, 0),
-    (fa.WAVE_BPERMUTE, fa.STAGE1_LDS, 512, 0),
-    (fa.WAVE_DPP, fa.STAGE1_FLAT, 512, 0),
-    (fa.WAVE_DPP, fa.STAGE1_FLAT, 64, 0),
-    (fa.WAVE_DPP, fa.STAGE1_FLAT, 1024, 0),
+    (fa.WAVE_BPERMUTE, fa.STAGE1_FLAT, 0, 0, 0),
+    (fa.WAVE_DPP, fa.STAGE1_LDS, 0, 0, 0),
+    (fa.WAVE_BPERMUTE, fa.STAGE1_LDS, 512, 0, fa.LOAD_STREAM),
+    (fa.WAVE_DPP, fa.STAGE1_FLAT, 512, 0, fa.LOAD_CACHED),
+    (fa.WAVE_DPP, fa.STAGE1_FLAT, 64, 0, fa.LOAD_STREAM),
+    (fa.WAVE_DPP, fa.STAGE1_FLAT, 1024, 0, 0),
+    (fa.WAVE_DPP, fa.STAGE1_FLAT, 0, 0, fa.LOAD_STREAM),
 ]
 
 
-@pytest.mark.parametrize("opt", OPTION_SETS, ids=lambda o: "w{}-s{}-b{}-p{}".format(*o))
+@pytest.mark.parametrize("opt", OPTION_SETS, ids=lambda o: "w{}-s{}-b{}-p{}-l{}".format(*o))
 @pytest.mark.parametrize("n,m,hidden", [(8, 37, 7168), (3, 11, 520), (5, 300, 2880), (1, 9, 64)])
 def test_design_options_are_bit_identical(opt, n, m, hidden):
     """The ds_bpermute wave reduction, the LDS-staged stage 1 and other stage-1 workgroup sizes
@@ -427,12 +428,13 @@ def test_randomized_shapes_paths_and_options():
         if (hidden // 8 + max(ppt, 1) - 1) // max(ppt, 1) > 1024:
             ppt = 0
         opt = fa.Options(int(rng.integers(0, 2)), int(rng.integers(0, 2)),
-                         int(rng.choice([0, 64, 256, 512, 1024])), ppt)
+                         int(rng.choice([0, 64, 256, 512, 1024])), ppt, int(rng.integers(0, 3)))
         eps = float(rng.choice([1e-6, 1e-5, 0.1]))
         dist = "stress" if rng.random() < 0.3 else "normal"
         p = synth.make_problem(n, m, hidden, seed=5000 + case, eps=eps, dist=dist, name="random")
         name = (f"random case {case}: n={n} m={m} hidden={hidden} path={path} "
-                f"options=({opt.wave_reduce},{opt.stage1},{opt.stage1_block},{opt.packs_per_thread}) "
+                f"options=({opt.wave_reduce},{opt.stage1},{opt.stage1_block},{opt.packs_per_thread},"
+                f"{opt.load_policy}) "
                 f"eps={eps} {dist}")
         announce(name)
         ins = [dev(x) for x in p.inputs]
