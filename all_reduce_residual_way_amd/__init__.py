@@ -70,7 +70,6 @@ def library():
         if not os.path.exists(LIBRARY_PATH):
             raise RuntimeError(
                 f"{LIBRARY_PATH} is not built; build it with "
-                "`python -c 'import __graft_entry__ as g; g.build()'` or "
                 "`python all_reduce_residual_way_amd/build.py`")
         lib = ctypes.CDLL(LIBRARY_PATH)
         lib.fused_ar_rmsnorm.argtypes = [ctypes.POINTER(_VP), ctypes.c_int, _VP, _VP, ctypes.c_float,

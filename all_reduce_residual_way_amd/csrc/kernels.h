@@ -196,7 +196,7 @@ __global__ void __launch_bounds__(1024) k_flat_reduce(FlatArgs a)
     }
 }
 
-// Stage 1 with LDS staging, one wave per input (the "warp-per-rank" design that the flat reduce
+// Stage 1 with LDS staging, one wave per input (the one-wave-per-rank design that the flat reduce
 // replaced: aiter PR #3817, Technical Details > 2stage > reduce-scatter), kept for comparison.
 // The page describes it only as staging through LDS with a workgroup barrier, one wave per rank;
 // this is a reading of that: a workgroup of N waves owns a tile of 64 * N packs; wave w copies

@@ -61,10 +61,16 @@ def parse_args():
 
 
 def kernel_source_digest():
+    """SHA-256 of the kernel and launch-plan sources with comments and whitespace removed: any
+    change to the code changes it, edits to comments do not."""
+    import re
     h = hashlib.sha256()
     for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

@@ -111,7 +111,7 @@ enum {
                                     DPP tree replaced (aiter PR #3817, Technical Details > 1stage) */
     FUSED_AR_STAGE1_FLAT = 0,    /* stage 1: one thread per pack, no LDS, no barrier (the default) */
     FUSED_AR_STAGE1_LDS = 1      /* stage 1: one wave per input staging a tile through LDS, one
-                                    barrier: the "warp-per-rank" design the flat reduce replaced
+                                    barrier: the one-wave-per-rank design the flat reduce replaced
                                     (aiter PR #3817, Technical Details > 2stage > reduce-scatter) */
 };
 
@@ -158,8 +158,8 @@ int fused_ar_rmsnorm_check(const fa_bf16 *const *inputs, int n, const fa_bf16 *r
                            const fa_bf16 *residual_out, const fa_bf16 *out, int path);
 
 /*
- * fused_ar_reduce - the reduce alone, the two-stage path's first kernel ("a flat reduce-scatter":
- * aiter PR #3817, Technical Details > 2stage > reduce-scatter): one thread per 8-element pack,
+ * fused_ar_reduce - the reduce alone, the two-stage path's first kernel, flat as in aiter PR #3817,
+ * Technical Details > 2stage > reduce-scatter: one thread per 8-element pack,
  * fp32 sum over the n inputs in array order, one bf16 store; no LDS, no workgroup barrier.
  *
  *   inputs   host array of n device pointers, each m * hidden bf16 (contiguous).

@@ -33,8 +33,8 @@
  * exact result to within binary64 rounding (see the comments at each step).
  *
  * Rounding to bf16 is round-to-nearest, ties to even, with overflow to infinity, subnormals kept
- * and NaN returned as a quiet NaN with the operand's sign. The pages only say "downcasts"; this is
- * the IEEE default rounding.
+ * and NaN returned as a quiet NaN with the operand's sign. The pages name no rounding mode for the
+ * conversion; this is the IEEE default.
  *
  * Layout: every [m, hidden] array is row-major and contiguous; bf16 values travel as their raw
  * 16-bit patterns (uint16_t).

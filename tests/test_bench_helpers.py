@@ -34,3 +34,19 @@ def test_parity_rows_stay_in_range():
         rows = bench.parity_rows(m)
         assert rows.min() == 0 and rows.max() == m - 1 and len(set(rows.tolist())) == len(rows)
     assert bench.parity_rows(1).tolist() == [0]
+
+
+def test_digest_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    copies = []
+    for i, path in enumerate(bench.KERNEL_SOURCES):
+        dst = tmp_path / f"src{i}"
+        dst.write_text(open(path).read())
+        copies.append(str(dst))
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", copies)
+    base = bench.kernel_source_digest()
+    with open(copies[0], "a") as f:
+        f.write("\n// a comment\n/* another\n   comment */\n")
+    assert bench.kernel_source_digest() == base
+    with open(copies[0], "a") as f:
+        f.write("\nstatic int extra_symbol = 1;\n")
+    assert bench.kernel_source_digest() != base
