@@ -99,7 +99,9 @@ __device__ __forceinline__ u32x4 load_once(const char *base, uint32_t off)
 //              comparison with the design the pages replaced).
 //   kResidual  false: a plain RMSNorm of in[0] (N == 1), with no residual and no residual_out;
 //              the last kernel of the unfused sequence.
-//   kStream    non-temporal loads of the inputs and the residual (see load_once).
+//   kStream    non-temporal loads of the inputs and the residual (see load_once); with N == 1 the
+//              input is the reduced rows the flat reduce has just stored (two-stage path, unfused
+//              sequence), which may still be in the Infinity Cache, so it is always loaded normally.
 template <int N, int PPT, bool kBpermute, bool kResidual, bool kStream>
 __global__ void __launch_bounds__(1024) k_rows(RowArgs a)
 {
@@ -129,7 +131,7 @@ __global__ void __launch_bounds__(1024) k_rows(RowArgs a)
             u32x4 x[N];
 #pragma unroll
             for (int i = 0; i < N; ++i)
-                x[i] = load_once<kStream>(in[i], off);
+                x[i] = (N == 1) ? load_pack(in[i], off) : load_once<kStream>(in[i], off);
             u32x4 res;
             if constexpr (kResidual)
                 res = load_once<kStream>(residual, off);
@@ -187,12 +189,9 @@ __global__ void __launch_bounds__(1024) k_flat_reduce(FlatArgs a)
         for (int i = 0; i < N; ++i)
             x[i] = load_once<kStream>(reinterpret_cast<const char *>(a.in[i]) + bytes, off);
         __builtin_amdgcn_sched_barrier(0);  // all N loads in flight before the first add
-        // the reduced rows are read back by the next kernel: cached unless streaming
-        const u32x4 r = narrow(reduce_packs<N>(x));
-        if constexpr (kStream)
-            store_stream(reinterpret_cast<char *>(a.out) + bytes, off, r);
-        else
-            store_pack(reinterpret_cast<char *>(a.out) + bytes, off, r);
+        // the reduced rows are read straight back by the next kernel: an ordinary store, so that
+        // they can stay in the Infinity Cache
+        store_pack(reinterpret_cast<char *>(a.out) + bytes, off, narrow(reduce_packs<N>(x)));
     }
 }
 
@@ -223,12 +222,8 @@ __global__ void __launch_bounds__(64 * N) k_stage1_lds(FlatArgs a)
 #pragma unroll
         for (int i = 0; i < N; ++i)
             x[i] = tile[i][t];
-        const u32x4 r = narrow(reduce_packs<N>(x));
-        char *dst = reinterpret_cast<char *>(a.out) + first * sizeof(u32x4);
-        if constexpr (kStream)
-            store_stream(dst, (uint32_t)t * sizeof(u32x4), r);
-        else
-            store_pack(dst, (uint32_t)t * sizeof(u32x4), r);
+        store_pack(reinterpret_cast<char *>(a.out) + first * sizeof(u32x4),
+                   (uint32_t)t * sizeof(u32x4), narrow(reduce_packs<N>(x)));
     }
 }
 
