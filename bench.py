@@ -204,6 +204,50 @@ def parity_rows(m):
     return rows
 
 
+def host_threads():
+    """Host threads this process may use, at most 16 (one GPU's share of a shared host)."""
+    try:
+        have = len(os.sched_getaffinity(0))
+    except AttributeError:
+        have = os.cpu_count() or 1
+    return max(1, min(16, have))
+
+
+def oracle_all_cores(oracle, prob, eps, bytes_alg, seconds):
+    """The unchanged oracle on row slices, one slice per host thread (ctypes drops the GIL).
+
+    Rows are independent, so the slices together give exactly the single-threaded result; the
+    first pass is checked against one single-threaded pass of the same rows.
+    """
+    import concurrent.futures as cf
+    import numpy as np
+    threads = host_threads()
+    m = prob.residual.shape[0]
+    bounds = [(m * t // threads, m * (t + 1) // threads) for t in range(threads)]
+    bounds = [(a, b) for a, b in bounds if b > a]
+
+    def piece(ab):
+        a, b = ab
+        return oracle.fused([x[a:b] for x in prob.inputs], prob.residual[a:b], prob.weight, eps)
+
+    with cf.ThreadPoolExecutor(len(bounds)) as pool:
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            parts = list(pool.map(piece, bounds))
+            passes += 1
+            elapsed = time.perf_counter() - t0
+            if passes == 1:
+                first = parts
+            if elapsed >= seconds:
+                break
+    a, b = bounds[0]
+    ro1, out1 = oracle.fused([x[a:b] for x in prob.inputs], prob.residual[a:b], prob.weight, eps)
+    same = bool(np.array_equal(first[0][0], ro1) and np.array_equal(first[0][1], out1))
+    return {"value": round(passes * bytes_alg / elapsed / 1e9, 4), "unit": "GB/s",
+            "cores": len(bounds), "passes": passes, "seconds": round(elapsed, 2),
+            "first_slice_matches_single_thread": same}
+
+
 def per_rank_share(torch, fa, work, steps, warmup):
     """One rank's share of the two-stage path in an N-way tensor-parallel group, on local HBM:
     stage 1 reduces only this rank's 1/N slice of the packs (here the first m/N rows), stage 2
@@ -406,6 +450,8 @@ def main():
                "kind": "oracle",
                "sample": f"the whole timed workload (n={n}, m={m}, hidden={hidden}), {passes} "
                          f"pass(es) in {elapsed:.1f} s, single-threaded C oracle"}
+        if not args.no_extra:
+            extra["cpu_oracle_all_cores"] = oracle_all_cores(oracle, prob, eps, bytes_alg, args.cpu_seconds / 2)
 
     traffic = measured_traffic() if (n, m, hidden, path) == (8, 4096, 7168, 1) else None
     props = torch.cuda.get_device_properties(0)

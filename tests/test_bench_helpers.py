@@ -50,3 +50,21 @@ def test_digest_ignores_comments_but_not_code(tmp_path, monkeypatch):
     with open(copies[0], "a") as f:
         f.write("\nstatic int extra_symbol = 1;\n")
     assert bench.kernel_source_digest() != base
+
+
+def test_oracle_all_cores_matches_single_thread():
+    import numpy as np
+    import oracle
+    from all_reduce_residual_way_amd import synth
+    prob = synth.make_problem(4, 37, 64, seed=5)
+    got = bench.oracle_all_cores(oracle.default(), prob, prob.eps, 1000, 0.0)
+    assert got["first_slice_matches_single_thread"] and got["passes"] == 1
+    assert 1 <= got["cores"] <= 16
+    # the slices cover every row exactly once: reassemble and compare with one whole pass
+    m, threads = 37, got["cores"]
+    bounds = [(m * t // threads, m * (t + 1) // threads) for t in range(threads)]
+    parts = [oracle.fused([x[a:b] for x in prob.inputs], prob.residual[a:b], prob.weight, prob.eps)
+             for a, b in bounds if b > a]
+    whole = oracle.fused(prob.inputs, prob.residual, prob.weight, prob.eps)
+    assert np.array_equal(np.concatenate([p[0] for p in parts]), whole[0])
+    assert np.array_equal(np.concatenate([p[1] for p in parts]), whole[1])
