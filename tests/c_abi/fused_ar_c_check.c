@@ -14,7 +14,8 @@
 
 #include "fused_ar.h"
 
-/* The oracle library's entry point (oracle/fused_ar_oracle.c); it has no header of its own. */
+/* The oracle library's entry points (oracle/fused_ar_oracle.c); it has no header of its own. */
+int oracle_reduce(const uint16_t *const *inputs, int n, long long count, uint16_t *reduced);
 int oracle_fused_ar_rmsnorm(const uint16_t *const *inputs, int n, const uint16_t *residual,
                             const uint16_t *weight, float eps, int m, int hidden,
                             uint16_t *residual_out, uint16_t *out);
@@ -155,31 +156,67 @@ static int gpu_checks(void)
     const fa_bf16 *ins[N];
     for (int i = 0; i < N; ++i)
         ins[i] = (const fa_bf16 *)d_in[i];
-    for (int variant = 0; variant < 3; ++variant) {
-        HIP_OK(hipMemset(d_ro, 0xFF, plane * 2));
-        HIP_OK(hipMemset(d_out, 0xFF, plane * 2));
-        HIP_OK(hipDeviceSynchronize());
-        int rc;
-        if (variant < 2)
-            rc = fused_ar_rmsnorm(ins, N, d_res, d_w, eps, M, H, d_ro, d_out, variant + 1, NULL);
-        else
-            rc = fused_ar_unfused_rmsnorm(ins, N, d_res, d_w, eps, M, H, d_ro, d_out, NULL);
-        CHECK(rc == FUSED_AR_OK);
-        HIP_OK(hipDeviceSynchronize());
-        HIP_OK(hipMemcpy(got_ro, d_ro, plane * 2, hipMemcpyDeviceToHost));
-        HIP_OK(hipMemcpy(got_out, d_out, plane * 2, hipMemcpyDeviceToHost));
-        for (size_t j = 0; j < plane; ++j) {
-            if (got_ro[j] != want_ro[j]) {
-                fprintf(stderr, "variant %d: residual_out[%zu] = %#06x, oracle %#06x\n", variant, j,
-                        got_ro[j], want_ro[j]);
-                return 1;
+    /* variants 0-2: path 1, path 2 and the unfused sequence on the null stream; 3-4: paths 1 and 2
+       captured from a stream of the caller's into a HIP graph, the graph replayed three times */
+    hipStream_t stream;
+    HIP_OK(hipStreamCreate(&stream));
+    for (int variant = 0; variant < 5; ++variant) {
+        hipGraph_t graph = NULL;
+        hipGraphExec_t exec = NULL;
+        if (variant >= 3) {
+            HIP_OK(hipStreamBeginCapture(stream, hipStreamCaptureModeGlobal));
+            const int rc = fused_ar_rmsnorm(ins, N, d_res, d_w, eps, M, H, d_ro, d_out, variant - 2,
+                                            stream);
+            HIP_OK(hipStreamEndCapture(stream, &graph));
+            CHECK(rc == FUSED_AR_OK);
+            HIP_OK(hipGraphInstantiate(&exec, graph, NULL, NULL, 0));
+        }
+        for (int replay = 0; replay < (variant >= 3 ? 3 : 1); ++replay) {
+            HIP_OK(hipMemset(d_ro, 0xFF, plane * 2));
+            HIP_OK(hipMemset(d_out, 0xFF, plane * 2));
+            HIP_OK(hipDeviceSynchronize());
+            int rc = FUSED_AR_OK;
+            if (variant < 2)
+                rc = fused_ar_rmsnorm(ins, N, d_res, d_w, eps, M, H, d_ro, d_out, variant + 1, NULL);
+            else if (variant == 2)
+                rc = fused_ar_unfused_rmsnorm(ins, N, d_res, d_w, eps, M, H, d_ro, d_out, NULL);
+            else
+                HIP_OK(hipGraphLaunch(exec, stream));
+            CHECK(rc == FUSED_AR_OK);
+            HIP_OK(hipDeviceSynchronize());
+            HIP_OK(hipMemcpy(got_ro, d_ro, plane * 2, hipMemcpyDeviceToHost));
+            HIP_OK(hipMemcpy(got_out, d_out, plane * 2, hipMemcpyDeviceToHost));
+            for (size_t j = 0; j < plane; ++j) {
+                if (got_ro[j] != want_ro[j]) {
+                    fprintf(stderr, "variant %d replay %d: residual_out[%zu] = %#06x, oracle %#06x\n",
+                            variant, replay, j, got_ro[j], want_ro[j]);
+                    return 1;
+                }
+                const int d = ordinal(got_out[j]) - ordinal(want_out[j]);
+                if (d > 1 || d < -1) {
+                    fprintf(stderr, "variant %d replay %d: out[%zu] = %#06x, oracle %#06x\n",
+                            variant, replay, j, got_out[j], want_out[j]);
+                    return 1;
+                }
             }
-            const int d = ordinal(got_out[j]) - ordinal(want_out[j]);
-            if (d > 1 || d < -1) {
-                fprintf(stderr, "variant %d: out[%zu] = %#06x, oracle %#06x\n", variant, j,
-                        got_out[j], want_out[j]);
-                return 1;
-            }
+        }
+        if (exec != NULL) {
+            HIP_OK(hipGraphExecDestroy(exec));
+            HIP_OK(hipGraphDestroy(graph));
+        }
+    }
+    HIP_OK(hipStreamDestroy(stream));
+
+    /* the reduce alone, bit-exact against the oracle's */
+    CHECK(oracle_reduce((const uint16_t *const *)h_in, N, (long long)plane, want_ro) == 0);
+    HIP_OK(hipMemset(d_ro, 0xFF, plane * 2));
+    CHECK(fused_ar_reduce(ins, N, M, H, d_ro, NULL) == FUSED_AR_OK);
+    HIP_OK(hipDeviceSynchronize());
+    HIP_OK(hipMemcpy(got_ro, d_ro, plane * 2, hipMemcpyDeviceToHost));
+    for (size_t j = 0; j < plane; ++j) {
+        if (got_ro[j] != want_ro[j]) {
+            fprintf(stderr, "reduce[%zu] = %#06x, oracle %#06x\n", j, got_ro[j], want_ro[j]);
+            return 1;
         }
     }
     for (int i = 0; i < N; ++i) {
@@ -191,7 +228,7 @@ static int gpu_checks(void)
     HIP_OK(hipFree(d_ro));
     HIP_OK(hipFree(d_out));
     free(h_res); free(h_w); free(want_ro); free(want_out); free(got_ro); free(got_out);
-    printf("gpu checks passed: path 1, path 2 and unfused match the oracle\n");
+    printf("gpu checks passed: path 1, path 2 and unfused (eager and graph-captured) and the reduce match the oracle\n");
     return 0;
 }
 
