@@ -392,7 +392,7 @@ int execute(const Plan &plan, const fa_bf16 *const *inputs, int n, const fa_bf16
     a.residual_out = ro;
     a.out = o;
     a.eps = eps;
-    a.hidden = static_cast<float>(hidden);
+    a.inv_hidden = static_cast<float>(1.0 / hidden);
     a.packs = packs;
 
     if (plan.path == FUSED_AR_PATH_ONESTAGE) {

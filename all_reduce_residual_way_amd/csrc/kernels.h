@@ -31,7 +31,7 @@ struct RowArgs {
     u32x4 *residual_out;          // [m, packs]; may equal residual
     u32x4 *out;                   // [m, packs]; may equal in[0] when N == 1 (stage 2)
     float eps;
-    float hidden;                 // row length as a float, the divisor of the mean
+    float inv_hidden;             // 1 / hidden rounded to fp32: the mean is the square-sum times it
     int packs;                    // packs per row = hidden / 8
 };
 
@@ -50,6 +50,16 @@ __device__ __forceinline__ F8 reduce_packs(const u32x4 (&x)[N])
     for (int i = 1; i < N; ++i)
         add_into(acc, widen(x[i]));
     return acc;
+}
+
+// 1 / sqrt(v) for v >= 0 by the hardware reciprocal square root (v_rsq_f32, within 1 ulp in
+// fp32). Below the normal range v is scaled by 2^24 first (and the result by 2^12), so subnormal
+// arguments, possible only with eps = 0 or eps subnormal, keep the same accuracy; 0 gives +inf.
+__device__ __forceinline__ float rsqrt_f32(float v)
+{
+    if (v >= 0x1p-126f)
+        return __builtin_amdgcn_rsqf(v);
+    return 0x1p12f * __builtin_amdgcn_rsqf(v * 0x1p24f);
 }
 
 // A pack at a byte offset from a wave-uniform base (the base stays in scalar registers, the
@@ -122,6 +132,7 @@ __global__ void __launch_bounds__(1024) k_rows(RowArgs a)
 
     u32x4 ro[PPT];
     u32x4 w[PPT];
+    F8 y1;  // one pack per thread: residual_out widened once, kept for the normalisation
     float ss = 0.0f;
 #pragma unroll
     for (int k = 0; k < PPT; ++k) {
@@ -147,6 +158,8 @@ __global__ void __launch_bounds__(1024) k_rows(RowArgs a)
                 ro[k] = x[0];
             }
             const F8 y = widen(ro[k]);
+            if constexpr (PPT == 1)
+                y1 = y;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 ss = __builtin_fmaf(y.v[e], y.v[e], ss);  // y * y is exact in fp32
@@ -154,14 +167,15 @@ __global__ void __launch_bounds__(1024) k_rows(RowArgs a)
     }
 
     const float total = block_sum<kBpermute>(ss, slots);
-    const float rstd = 1.0f / __builtin_sqrtf(total / a.hidden + a.eps);
+    const float rstd = rsqrt_f32(total * a.inv_hidden + a.eps);
 
 #pragma unroll
     for (int k = 0; k < PPT; ++k) {
         const uint32_t p = tid + k * nthreads;
         if (p < packs) {
             const uint32_t off = p * (uint32_t)sizeof(u32x4);
-            const F8 y = widen(ro[k]);
+            // with more packs per thread, widening again costs fewer registers than keeping them
+            const F8 y = PPT == 1 ? y1 : widen(ro[k]);
             const F8 g = widen(w[k]);
             F8 o;
 #pragma unroll

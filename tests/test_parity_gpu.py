@@ -243,6 +243,22 @@ def test_eps_values(eps):
         check_problem(p, path)
 
 
+@pytest.mark.parametrize("eps", [0.0, 1e-44])
+def test_tiny_rows_with_subnormal_mean_square(eps):
+    """Rows scaled by 2^-60 .. 2^-68, so that mean(x^2) + eps falls from the normal range (1e-36)
+    into fp32's subnormals (down to 3e-41) with eps = 0 or subnormal: the reciprocal square root
+    must stay accurate there."""
+    rng = np.random.default_rng(31)
+    scales = [2.0 ** -60, 2.0 ** -63, 2.0 ** -66, 2.0 ** -68]
+    inputs = [synth.to_bf16_bits(np.array([rng.standard_normal(64) * s for s in scales],
+                                          dtype=np.float32)) for _ in range(2)]
+    residual = np.zeros((len(scales), 64), dtype=np.uint16)
+    weight = synth.to_bf16_bits((1 + 0.1 * rng.standard_normal(64)).astype(np.float32))
+    p = synth.Problem(inputs, residual, weight, eps, name=f"tiny rows eps={eps}")
+    for path in (1, 2):
+        check_problem(p, path)
+
+
 def test_large_values_and_ties():
     """The stress mix: +-3e4 rows, whose sums land on bf16 rounding ties."""
     p = synth.make_problem(8, 300, 2880, seed=11, dist="stress", name="stress ties")
