@@ -20,7 +20,7 @@ constexpr int kPackElems = 8;
 constexpr int kMaxBlock = 1024;
 constexpr unsigned kFlatBlock = 256;              // stage-1 workgroup (aiter PR #3817, 2stage >
                                                   // stage-1 launch config)
-constexpr size_t kFlatMaxGrid = size_t(1) << 22;  // beyond this the flat kernel strides
+constexpr size_t kFlatPacksPerLaunch = size_t(1) << 30;  // more packs take several launches
 constexpr int kRowsPerLaunch = 1 << 20;           // taller problems take several launches
 constexpr int kPathUnfusedPlan = 3;               // internal plan id of the unfused sequence
 
@@ -270,15 +270,15 @@ struct Plan {
     Step step[3];
 };
 
+// A flat kernel over total_packs packs, one per thread, in launches of at most
+// kFlatPacksPerLaunch packs; `grid` is that of the first launch.
 Step flat_step(const void *kernel, const char *name, int n, size_t total_packs, unsigned block,
                bool stream)
 {
-    size_t g = (total_packs + block - 1) / block;
-    if (g > kFlatMaxGrid)
-        g = kFlatMaxGrid;
-    const size_t covered = g * block;
-    return {kernel, name, static_cast<unsigned>(g), block,
-            static_cast<unsigned>((total_packs + covered - 1) / covered), 1, n, stream};
+    const size_t first = total_packs < kFlatPacksPerLaunch ? total_packs : kFlatPacksPerLaunch;
+    const size_t launches = (total_packs + kFlatPacksPerLaunch - 1) / kFlatPacksPerLaunch;
+    return {kernel, name, static_cast<unsigned>((first + block - 1) / block), block, 1,
+            static_cast<unsigned>(launches), n, stream};
 }
 
 // The launches of one call along `path` (one-stage, two-stage or the unfused sequence).
@@ -307,12 +307,8 @@ int make_plan(int n, int m, int hidden, int path, const Options &o, Plan *plan)
         return FUSED_AR_OK;
     }
     if (o.lds_stage1) {
-        const unsigned block = 64u * static_cast<unsigned>(n);
-        const size_t g = (total + block - 1) / block;
-        if (g > 0x7FFFFFFFu / block)
-            return FUSED_AR_ERR_SHAPE;  // the LDS-staged kernel does not stride
-        plan->step[0] = {lds_kernel(n, stream), "stage1_reduce_lds", static_cast<unsigned>(g),
-                         block, 1, 1, n, stream};
+        plan->step[0] = flat_step(lds_kernel(n, stream), "stage1_reduce_lds", n, total,
+                                  64u * static_cast<unsigned>(n), stream);
     } else {
         plan->step[0] = flat_step(flat_kernel(n, stream), "stage1_reduce", n, total, o.flat_block,
                                   stream);
@@ -362,15 +358,24 @@ int run_rows(const Step &s, const RowArgs &args, int m, int packs, hipStream_t s
     return FUSED_AR_OK;
 }
 
+// At most kFlatPacksPerLaunch packs per launch; later launches start that many packs further into
+// every buffer.
 int run_flat(const Step &s, const u32x4 *const *inputs, size_t total_packs, u32x4 *dst,
              hipStream_t stream)
 {
-    FlatArgs a{};
-    for (int i = 0; i < s.n; ++i)
-        a.in[i] = inputs[i];
-    a.out = dst;
-    a.total_packs = total_packs;
-    return launch(s.kernel, s.grid, s.block, &a, stream);
+    for (size_t first = 0; first < total_packs; first += kFlatPacksPerLaunch) {
+        const size_t left = total_packs - first;
+        FlatArgs a{};
+        for (int i = 0; i < s.n; ++i)
+            a.in[i] = inputs[i] + first;
+        a.out = dst + first;
+        a.packs = static_cast<uint32_t>(left < kFlatPacksPerLaunch ? left : kFlatPacksPerLaunch);
+        const unsigned grid = (a.packs + s.block - 1) / s.block;
+        const int rc = launch(s.kernel, grid, s.block, &a, stream);
+        if (rc != FUSED_AR_OK)
+            return rc;
+    }
+    return FUSED_AR_OK;
 }
 
 // Runs a validated call (m > 0) along `plan`.

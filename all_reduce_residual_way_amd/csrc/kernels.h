@@ -38,7 +38,7 @@ struct RowArgs {
 struct FlatArgs {
     const u32x4 *in[kMaxInputs];
     u32x4 *out;
-    size_t total_packs;
+    uint32_t packs;  // packs in this launch (the host splits larger problems into launches)
 };
 
 // Sum of the N packs in input order, in fp32, starting from input 0.
@@ -186,27 +186,24 @@ __global__ void __launch_bounds__(1024) k_rows(RowArgs a)
     }
 }
 
-// Flat N-way reduce: workgroup b handles the blockDim.x packs starting at pack b * blockDim.x,
-// then strides by the whole grid (one pass when the grid covers the problem, which it does up to
-// 2^30 packs).
+// Flat N-way reduce: thread t of workgroup b handles pack b * blockDim.x + t (one pack per thread;
+// the host launches enough workgroups, splitting more than 2^30 packs into several launches).
 template <int N, bool kStream>
 __global__ void __launch_bounds__(1024) k_flat_reduce(FlatArgs a)
 {
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    const uint32_t first = blockIdx.x * blockDim.x;
+    if (first + threadIdx.x >= a.packs)
+        return;
+    const size_t bytes = (size_t)first * sizeof(u32x4);
     const uint32_t off = threadIdx.x * (uint32_t)sizeof(u32x4);
-    for (size_t first = (size_t)blockIdx.x * blockDim.x; first < a.total_packs; first += stride) {
-        if (first + threadIdx.x >= a.total_packs)
-            break;
-        const size_t bytes = first * sizeof(u32x4);
-        u32x4 x[N];
+    u32x4 x[N];
 #pragma unroll
-        for (int i = 0; i < N; ++i)
-            x[i] = load_once<kStream>(reinterpret_cast<const char *>(a.in[i]) + bytes, off);
-        __builtin_amdgcn_sched_barrier(0);  // all N loads in flight before the first add
-        // the reduced rows are read straight back by the next kernel: an ordinary store, so that
-        // they can stay in the Infinity Cache
-        store_pack(reinterpret_cast<char *>(a.out) + bytes, off, narrow(reduce_packs<N>(x)));
-    }
+    for (int i = 0; i < N; ++i)
+        x[i] = load_once<kStream>(reinterpret_cast<const char *>(a.in[i]) + bytes, off);
+    __builtin_amdgcn_sched_barrier(0);  // all N loads in flight before the first add
+    // the reduced rows are read straight back by the next kernel: an ordinary store, so that they
+    // can stay in the Infinity Cache
+    store_pack(reinterpret_cast<char *>(a.out) + bytes, off, narrow(reduce_packs<N>(x)));
 }
 
 // Stage 1 with LDS staging, one wave per input (the one-wave-per-rank design that the flat reduce
@@ -219,19 +216,21 @@ template <int N, bool kStream>
 __global__ void __launch_bounds__(64 * N) k_stage1_lds(FlatArgs a)
 {
     __shared__ u32x4 tile[N][64 * N];
-    const int wave = threadIdx.x >> 6;
+    // the wave index is uniform across the wave: reading it from lane 0 lets the compiler keep
+    // the wave's input pointer in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const size_t first = (size_t)blockIdx.x * (64 * N);
     const char *src = reinterpret_cast<const char *>(a.in[wave]);
 #pragma unroll
     for (int j = 0; j < N; ++j) {
         const int q = j * 64 + lane;
-        if (first + q < a.total_packs)
+        if (first + q < a.packs)
             tile[wave][q] = load_once<kStream>(src + first * sizeof(u32x4), (uint32_t)q * sizeof(u32x4));
     }
     __syncthreads();
     const int t = threadIdx.x;
-    if (first + t < a.total_packs) {
+    if (first + t < a.packs) {
         u32x4 x[N];
 #pragma unroll
         for (int i = 0; i < N; ++i)

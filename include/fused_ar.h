@@ -187,9 +187,9 @@ typedef struct {
                              "stage2_norm", "residual_add" or "rmsnorm" */
     unsigned grid;        /* workgroups per launch (the row kernels: one per row) */
     unsigned block;       /* threads per workgroup (a multiple of 64) */
-    unsigned per_thread;  /* 8-element packs each thread handles per row (or per stride) */
-    unsigned launches;    /* launches of this kernel per call (rows come in launches of at most
-                             2^20 workgroups) */
+    unsigned per_thread;  /* 8-element packs each thread handles per row (1 in flat kernels) */
+    unsigned launches;    /* launches of this kernel per call: rows come in launches of at most
+                             2^20 workgroups, flat kernels' packs in launches of at most 2^30 */
     unsigned streaming;   /* 1: non-temporal loads of the inputs; 0: ordinary loads */
 } fused_ar_kernel_launch;
 

@@ -287,6 +287,25 @@ def test_rows_beyond_the_grid():
         assert_parity("row stride", ro[rows], out[rows], want_ro, want_out)
 
 
+def test_flat_packs_beyond_one_launch():
+    """More packs than one flat launch takes (2^30): the reduce comes in two launches, the second
+    starting 2^30 packs into every buffer. With one input the reduce is the identity on finite
+    values, so every element of the 16 GiB plane is checked, on the GPU."""
+    m, hidden = (1 << 18) + 1, 32768   # 2^30 + 4096 packs of 8 elements
+    assert fa.describe_launch(1, m, hidden, 2)["kernels"][0]["launches"] == 2
+    announce(f"flat launches: reduce n=1 m={m} hidden={hidden}")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(17)
+    x = torch.randint(0, 0x7F80, (m, hidden), dtype=torch.int16, device="cuda", generator=gen)
+    red = fa.fused_ar_reduce([x.view(torch.bfloat16)])
+    torch.cuda.synchronize()
+    red = red.view(torch.int16)
+    for r in range(0, m, 8192):
+        assert torch.equal(red[r:r + 8192], x[r:r + 8192]), r
+    del x, red
+    torch.cuda.empty_cache()
+
+
 def test_empty_problem():
     x = torch.empty(0, 4096, dtype=torch.bfloat16, device="cuda")
     w = torch.ones(4096, dtype=torch.bfloat16, device="cuda")
