@@ -403,7 +403,7 @@ def main():
         designs = {
             "onestage_dpp": (1, None),
             "onestage_bpermute": (1, fa.Options(fa.WAVE_BPERMUTE, 0, 0, 0)),
-            "twostage_flat_256": (2, None),
+            "twostage_flat_256": (2, fa.Options(0, fa.STAGE1_FLAT, 256, 0)),
             "twostage_flat_512": (2, fa.Options(0, fa.STAGE1_FLAT, 512, 0)),
             "twostage_lds_staged": (2, fa.Options(0, fa.STAGE1_LDS, 0, 0)),
         }
@@ -425,7 +425,8 @@ def main():
                     "onestage_dpp": decode[str(dm)],
                     "onestage_bpermute": round(dw.graph_latency_us(
                         1, fa.Options(fa.WAVE_BPERMUTE, 0, 0, 0)), 3),
-                    "twostage_flat_256": round(dw.graph_latency_us(2), 3),
+                    "twostage_flat_256": round(dw.graph_latency_us(
+                        2, fa.Options(0, fa.STAGE1_FLAT, 256, 0)), 3),
                     "twostage_flat_512": round(dw.graph_latency_us(
                         2, fa.Options(0, fa.STAGE1_FLAT, 512, 0)), 3),
                     "twostage_lds_staged": round(dw.graph_latency_us(

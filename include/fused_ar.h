@@ -126,8 +126,9 @@ enum {
 typedef struct {
     int wave_reduce;       /* FUSED_AR_WAVE_DPP or FUSED_AR_WAVE_BPERMUTE */
     int stage1;            /* FUSED_AR_STAGE1_FLAT or FUSED_AR_STAGE1_LDS */
-    int stage1_block;      /* threads per workgroup of the flat kernels: 0 = 256 (aiter PR #3817,
-                              2stage > stage-1 launch config), else a multiple of 64 in [64, 1024] */
+    int stage1_block;      /* threads per workgroup of the flat kernels: 0 = by size, 256 (aiter
+                              PR #3817, 2stage > stage-1 launch config) below 2^20 packs and 512
+                              from there on; else a multiple of 64 in [64, 1024] */
     int packs_per_thread;  /* row kernels: 0 = automatic, else 1, 2 or 4 (FUSED_AR_ERR_SHAPE if the
                               row then needs more than 1024 threads) */
     int load_policy;       /* FUSED_AR_LOAD_AUTO, FUSED_AR_LOAD_CACHED or FUSED_AR_LOAD_STREAM: how

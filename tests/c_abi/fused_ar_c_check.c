@@ -65,16 +65,22 @@ static int cpu_checks(void)
     CHECK(fused_ar_describe_launch(8, 2147483647, 32768, FUSED_AR_PATH_UNFUSED, &plan) == FUSED_AR_OK);
     CHECK(plan.kernels == 3);
     CHECK(fused_ar_describe_launch(8, 2147483647, 32768, FUSED_AR_PATH_TWOSTAGE, &plan) == FUSED_AR_OK);
-    /* (2^31 - 1) * 4096 packs: 8192 flat launches of 2^30 packs (the last one short) */
-    CHECK(plan.launch[0].launches == 8192u && plan.launch[0].grid == (1u << 22) &&
-          plan.launch[0].per_thread == 1u);
+    /* (2^31 - 1) * 4096 packs: 8192 flat launches of 2^30 packs (the last one short), 512-thread
+       workgroups at this size */
+    CHECK(plan.launch[0].launches == 8192u && plan.launch[0].grid == (1u << 21) &&
+          plan.launch[0].block == 512u && plan.launch[0].per_thread == 1u);
     fused_ar_options lds = {FUSED_AR_WAVE_DPP, FUSED_AR_STAGE1_LDS, 0, 0, FUSED_AR_LOAD_STREAM};
     CHECK(fused_ar_describe_launch_ex(8, 2147483647, 32768, FUSED_AR_PATH_TWOSTAGE, &lds, &plan) ==
           FUSED_AR_OK);
     CHECK(plan.launch[0].launches == 8192u && plan.launch[0].grid == (1u << 21));
     /* 2^30 + 4096 packs: a second launch for the last row */
     CHECK(fused_ar_describe_launch(2, 262145, 32768, FUSED_AR_PATH_TWOSTAGE, &plan) == FUSED_AR_OK);
-    CHECK(plan.launch[0].launches == 2u && plan.launch[0].grid == (1u << 22));
+    CHECK(plan.launch[0].launches == 2u && plan.launch[0].grid == (1u << 21));
+    /* the flat workgroup: 256 threads below 2^20 packs, 512 from there on */
+    CHECK(fused_ar_describe_launch(8, 1023, 8192, FUSED_AR_PATH_TWOSTAGE, &plan) == FUSED_AR_OK);
+    CHECK(plan.launch[0].block == 256u && plan.launch[0].grid == 1023u * 4u);
+    CHECK(fused_ar_describe_launch(8, 1024, 8192, FUSED_AR_PATH_TWOSTAGE, &plan) == FUSED_AR_OK);
+    CHECK(plan.launch[0].block == 512u && plan.launch[0].grid == 1024u * 2u);
     CHECK(fused_ar_describe_launch(8, -2147483647 - 1, 8, 1, &plan) == FUSED_AR_ERR_INVALID);
     CHECK(fused_ar_describe_launch(8, 1, 2147483647, 1, &plan) == FUSED_AR_ERR_SHAPE);
     CHECK(fused_ar_describe_launch(8, 1, 2147483640, 1, &plan) == FUSED_AR_ERR_SHAPE);
