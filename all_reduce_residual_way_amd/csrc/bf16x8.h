@@ -1,9 +1,9 @@
 // bf16x8.h - the 16-byte "pack" of eight bf16 values that every kernel moves with one
 // global_load_dwordx4 / global_store_dwordx4, and its conversions to and from eight floats.
 //
-// The pack is the per-thread unit of the flat reduce ("each thread reduces one pack across all
-// input ranks": aiter PR #3817, Technical Details > 2stage > reduce-scatter); the page does not
-// give its width, and 16 bytes is the widest single vector memory access on gfx950.
+// The pack is the per-thread unit of the flat reduce, in which every thread sums one pack over all
+// the ranks' buffers (aiter PR #3817, Technical Details > 2stage > reduce-scatter); the page does
+// not give its width, and 16 bytes is the widest single vector memory access on gfx950.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -95,9 +95,10 @@ int fused_ar_rmsnorm(const fa_bf16 *const *inputs, int n, const fa_bf16 *residua
  * fused_ar_unfused_rmsnorm - the same result as fused_ar_rmsnorm, bit for bit, computed the way an
  * unfused epilogue would: an all-reduce (the flat reduce kernel) writing the reduced rows to
  * `out`, a residual add writing residual_out, then an RMSNorm kernel reading residual_out back and
- * writing out. The baseline that the fused paths are measured against ("the complete unfused
- * operation" that the tokenspeed PR #968 backend falls back to: Summary (AI); the unfused baseline
- * of its performance figures). It moves 2 (n + 6) m hidden bytes instead of 2 (n + 3) m hidden.
+ * writing out. The baseline that the fused paths are measured against: the tokenspeed PR #968
+ * backend falls back to the whole operation done unfused whenever it declines (Summary (AI)), and
+ * its performance figures compare against that. It moves 2 (n + 6) m hidden bytes instead of
+ * 2 (n + 3) m hidden.
  * Arguments, conventions and errors as for fused_ar_rmsnorm (no path argument).
  */
 int fused_ar_unfused_rmsnorm(const fa_bf16 *const *inputs, int n, const fa_bf16 *residual,

@@ -13,8 +13,8 @@
  * a residual [m, hidden] (bf16) and a weight [hidden] (bf16):
  *
  *   1. Reduce. "perf: optimize fused AllReduce + RMSNorm (custom_all_reduce)" (ROCm/aiter PR #3817),
- *      Technical Details > 2stage > reduce-scatter: every element is reduced across all input ranks
- *      in fp32, in the rank order ptrs[0..ngpus-1], and the fp32 result is downcast to bf16.
+ *      Technical Details > 2stage > reduce-scatter: each element is summed over the n buffers in
+ *      fp32, in the buffer order ptrs[0..ngpus-1], and the fp32 sum is rounded to bf16.
  *      The accumulator starts from the first rank's value and each further rank is added with
  *      one fp32 addition.
  *   2. Residual. "perf(comm): add opt-in Triton AR+RMSNorm backend" (lightseekorg/tokenspeed PR #968),
