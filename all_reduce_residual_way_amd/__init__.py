@@ -13,7 +13,8 @@ import os
 
 __all__ = [
     "FusedArError", "Options", "library", "fused_ar_rmsnorm", "fused_ar_unfused_rmsnorm",
-    "fused_ar_reduce", "fused_ar_rmsnorm_ptrs", "fused_ar_rmsnorm_ex_ptrs",
+    "fused_ar_reduce", "fused_ar_rmsnorm_split", "split_workspace_bytes",
+    "fused_ar_rmsnorm_split_ptrs", "fused_ar_rmsnorm_ptrs", "fused_ar_rmsnorm_ex_ptrs",
     "fused_ar_unfused_rmsnorm_ptrs", "fused_ar_reduce_ptrs", "fused_ar_rmsnorm_check_ptrs",
     "auto_path", "describe_launch", "strerror",
     "OK", "ERR_INVALID", "ERR_SHAPE", "ERR_ALIGN", "ERR_ALIAS",
@@ -99,6 +100,12 @@ def library():
         lib.fused_ar_describe_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                  ctypes.c_int, ctypes.POINTER(_LaunchPlan)]
         lib.fused_ar_describe_launch.restype = ctypes.c_int
+        lib.fused_ar_rmsnorm_split.argtypes = [ctypes.POINTER(_VP), ctypes.c_int, _VP, _VP,
+                                               ctypes.c_float, ctypes.c_int, ctypes.c_int, _VP,
+                                               _VP, ctypes.c_int, _VP, ctypes.c_size_t, _VP]
+        lib.fused_ar_rmsnorm_split.restype = ctypes.c_int
+        lib.fused_ar_split_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        lib.fused_ar_split_workspace_bytes.restype = ctypes.c_size_t
         lib.fused_ar_strerror.argtypes = [ctypes.c_int]
         lib.fused_ar_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -179,6 +186,21 @@ def fused_ar_reduce_ptrs(input_ptrs, m, hidden, reduced, stream=0):
     arr = _ptr_array(input_ptrs)
     return library().fused_ar_reduce(arr, len(input_ptrs), int(m), int(hidden), _VP(reduced),
                                      _VP(stream))
+
+
+def split_workspace_bytes(m, hidden, splits=0):
+    """Workspace bytes fused_ar_rmsnorm_split needs (0 for m == 0 or invalid scalars)."""
+    return int(library().fused_ar_split_workspace_bytes(int(m), int(hidden), int(splits)))
+
+
+def fused_ar_rmsnorm_split_ptrs(input_ptrs, residual, weight, eps, m, hidden, residual_out, out,
+                                splits, workspace, workspace_bytes, stream=0):
+    """Raw call of the split-row form; returns the status."""
+    arr = _ptr_array(input_ptrs)
+    return library().fused_ar_rmsnorm_split(arr, len(input_ptrs), _VP(residual), _VP(weight),
+                                            float(eps), int(m), int(hidden), _VP(residual_out),
+                                            _VP(out), int(splits), _VP(workspace),
+                                            int(workspace_bytes), _VP(stream))
 
 
 def _check_tensor(t, name, shape, device):
@@ -286,3 +308,28 @@ def fused_ar_reduce(inputs, *, reduced=None, stream=None):
     if rc != OK:
         raise FusedArError(rc, "fused_ar_reduce")
     return reduced
+
+
+def fused_ar_rmsnorm_split(inputs, residual, weight, eps=1e-6, *, splits=0, workspace=None,
+                           residual_out=None, out=None, stream=None):
+    """The one-stage result with each row cut into ``splits`` slices on separate workgroups (0 =
+    one slice per 256 packs), in two kernels. ``workspace`` is a CUDA tensor of at least
+    ``split_workspace_bytes(m, hidden, splits)`` bytes, allocated here when None. Other arguments
+    and returns as fused_ar_rmsnorm (always the one-stage path)."""
+    import torch
+    m, hidden, device, residual_out, out = _prepare(inputs, residual, weight, residual_out, out)
+    need = split_workspace_bytes(m, hidden, splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4) // 4, dtype=torch.float32, device=device)
+    if not isinstance(workspace, torch.Tensor) or workspace.device != device:
+        raise ValueError(f"workspace must be a tensor on {device}")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = fused_ar_rmsnorm_split_ptrs([x.data_ptr() for x in inputs], residual.data_ptr(),
+                                     weight.data_ptr(), eps, m, hidden, residual_out.data_ptr(),
+                                     out.data_ptr(), splits, workspace.data_ptr(), nbytes,
+                                     _stream_handle(stream, device))
+    if rc != OK:
+        raise FusedArError(rc, "fused_ar_rmsnorm_split")
+    return residual_out, out

@@ -268,6 +268,44 @@ const void *lds_kernel(int n, bool stream)
     return stream ? lds_kernel_s<true>(n) : lds_kernel_s<false>(n);
 }
 
+template <bool kS>
+const void *split_kernel_s(int n)
+{
+    switch (n) {
+    case 1: return reinterpret_cast<const void *>(&fa::k_split_reduce<1, kS>);
+    case 2: return reinterpret_cast<const void *>(&fa::k_split_reduce<2, kS>);
+    case 3: return reinterpret_cast<const void *>(&fa::k_split_reduce<3, kS>);
+    case 4: return reinterpret_cast<const void *>(&fa::k_split_reduce<4, kS>);
+    case 5: return reinterpret_cast<const void *>(&fa::k_split_reduce<5, kS>);
+    case 6: return reinterpret_cast<const void *>(&fa::k_split_reduce<6, kS>);
+    case 7: return reinterpret_cast<const void *>(&fa::k_split_reduce<7, kS>);
+    case 8: return reinterpret_cast<const void *>(&fa::k_split_reduce<8, kS>);
+    default: return nullptr;
+    }
+}
+
+// Slices per row of the split-row call: `splits` if given, else one slice per kSplitPacks packs.
+// Each slice takes one pack per thread, so a slice holds at most kMaxBlock packs.
+constexpr int kSplitPacks = 256;
+constexpr int kMaxSplits = 64;
+
+int split_geometry(int hidden, int splits, int *resolved, int *slice_packs, int *threads)
+{
+    const int packs = hidden / kPackElems;
+    int s = splits != 0 ? splits : (packs + kSplitPacks - 1) / kSplitPacks;
+    if (s < 1 || s > kMaxSplits)
+        return FUSED_AR_ERR_INVALID;
+    if (s > packs)
+        s = packs;  // no empty slices
+    const int sp = (packs + s - 1) / s;
+    if (sp > kMaxBlock)
+        return FUSED_AR_ERR_SHAPE;  // too few slices for one pack per thread
+    *resolved = s;
+    *slice_packs = sp;
+    *threads = (sp + 63) / 64 * 64;
+    return FUSED_AR_OK;
+}
+
 struct Step {
     const void *kernel;
     const char *name;
@@ -541,6 +579,81 @@ extern "C" int fused_ar_reduce(const fa_bf16 *const *inputs, int n, int m, int h
     const Step s = flat_step(flat_kernel(n, nt), "stage1_reduce", n, total_packs,
                              flat_block_for(kDefaultOptions, total_packs), nt);
     return run_flat(s, ins, total_packs, reinterpret_cast<u32x4 *>(reduced), stream);
+}
+
+extern "C" size_t fused_ar_split_workspace_bytes(int m, int hidden, int splits)
+{
+    if (m < 0 || hidden <= 0 || hidden % kPackElems != 0 || hidden > FUSED_AR_MAX_HIDDEN)
+        return 0;
+    int s, sp, threads;
+    if (split_geometry(hidden, splits, &s, &sp, &threads) != FUSED_AR_OK)
+        return 0;
+    return (size_t)m * (size_t)s * sizeof(float);
+}
+
+extern "C" int fused_ar_rmsnorm_split(const fa_bf16 *const *inputs, int n, const fa_bf16 *residual,
+                                      const fa_bf16 *weight, float eps, int m, int hidden,
+                                      fa_bf16 *residual_out, fa_bf16 *out, int splits,
+                                      void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    int rc = check_scalars(n, m, hidden, eps, FUSED_AR_PATH_ONESTAGE, true);
+    if (rc != FUSED_AR_OK)
+        return rc;
+    int s, slice_packs, threads;
+    rc = split_geometry(hidden, splits, &s, &slice_packs, &threads);
+    if (rc != FUSED_AR_OK || m == 0)
+        return rc;
+    rc = check_buffers(inputs, n, residual, weight, m, hidden, residual_out, out);
+    if (rc != FUSED_AR_OK)
+        return rc;
+    const size_t need = (size_t)m * (size_t)s * sizeof(float);
+    Span ws;
+    if (workspace == nullptr || workspace_bytes < need || !make_span(workspace, need, &ws))
+        return FUSED_AR_ERR_INVALID;
+    if (!aligned16(workspace))
+        return FUSED_AR_ERR_ALIGN;
+    const size_t plane = (size_t)m * (size_t)hidden * sizeof(fa_bf16);
+    Span other;
+    for (int i = 0; i < n; ++i)
+        if (make_span(inputs[i], plane, &other) && overlaps(ws, other))
+            return FUSED_AR_ERR_ALIAS;
+    const void *bufs[3] = {residual, residual_out, out};
+    for (const void *b : bufs)
+        if (make_span(b, plane, &other) && overlaps(ws, other))
+            return FUSED_AR_ERR_ALIAS;
+    if (make_span(weight, (size_t)hidden * sizeof(fa_bf16), &other) && overlaps(ws, other))
+        return FUSED_AR_ERR_ALIAS;
+
+    const int packs = hidden / kPackElems;
+    const bool stream_loads = use_stream(kDefaultOptions, n, m, hidden);
+    const void *reduce_kernel = stream_loads ? split_kernel_s<true>(n) : split_kernel_s<false>(n);
+    const void *norm_kernel = reinterpret_cast<const void *>(&fa::k_split_norm);
+    // rows in launches of at most kRowsPerLaunch, as for the row kernels
+    for (int64_t first = 0; first < m; first += kRowsPerLaunch) {
+        const int rows = static_cast<int>(m - first < kRowsPerLaunch ? m - first : kRowsPerLaunch);
+        const size_t skip = (size_t)first * (size_t)packs;  // in packs
+        fa::SplitArgs a{};
+        for (int i = 0; i < n; ++i)
+            a.r.in[i] = reinterpret_cast<const u32x4 *>(inputs[i]) + skip;
+        a.r.residual = reinterpret_cast<const u32x4 *>(residual) + skip;
+        a.r.weight = reinterpret_cast<const u32x4 *>(weight);
+        a.r.residual_out = reinterpret_cast<u32x4 *>(residual_out) + skip;
+        a.r.out = reinterpret_cast<u32x4 *>(out) + skip;
+        a.r.eps = eps;
+        a.r.inv_hidden = static_cast<float>(1.0 / hidden);
+        a.r.packs = packs;
+        a.partial = static_cast<float *>(workspace) + (size_t)first * (size_t)s;
+        a.splits = s;
+        a.slice_packs = slice_packs;
+        const unsigned grid = static_cast<unsigned>(rows) * static_cast<unsigned>(s);
+        rc = launch(reduce_kernel, grid, static_cast<unsigned>(threads), &a, stream);
+        if (rc != FUSED_AR_OK)
+            return rc;
+        rc = launch(norm_kernel, grid, static_cast<unsigned>(threads), &a, stream);
+        if (rc != FUSED_AR_OK)
+            return rc;
+    }
+    return FUSED_AR_OK;
 }
 
 extern "C" int fused_ar_describe_launch_ex(int n, int m, int hidden, int path,

@@ -206,6 +206,78 @@ __global__ void __launch_bounds__(1024) k_flat_reduce(FlatArgs a)
     store_pack(reinterpret_cast<char *>(a.out) + bytes, off, narrow(reduce_packs<N>(x)));
 }
 
+// Split rows: each row is cut into `splits` slices of slice_packs packs, one workgroup per slice,
+// so that a few rows still spread over many CUs. Two kernels on one stream: k_split_reduce writes
+// residual_out and each slice's square-sum into `partial`; k_split_norm sums a row's partials in
+// slice order (the same bits in every workgroup of the row) and normalises its slice. The second
+// launch is the combine; it needs no wait inside a kernel. Workgroup b of a launch handles slice
+// b % splits of row b / splits, one pack per thread.
+struct SplitArgs {
+    RowArgs r;        // the buffers, eps and row length, as for k_rows
+    float *partial;   // [rows, splits] square-sums of the slices: the caller's workspace
+    int splits;       // slices per row
+    int slice_packs;  // packs per slice (the last slice of a row may hold fewer)
+};
+
+template <int N, bool kStream>
+__global__ void __launch_bounds__(1024) k_split_reduce(SplitArgs a)
+{
+    __shared__ float slots[kMaxWaves];
+    const uint32_t splits = (uint32_t)a.splits;
+    const uint32_t row = blockIdx.x / splits;
+    const uint32_t slice = blockIdx.x - row * splits;
+    const uint32_t packs = (uint32_t)a.r.packs;
+    const uint32_t p = slice * (uint32_t)a.slice_packs + threadIdx.x;
+    const size_t row_bytes = (size_t)row * packs * sizeof(u32x4);
+    float ss = 0.0f;
+    if (threadIdx.x < (uint32_t)a.slice_packs && p < packs) {
+        const uint32_t off = p * (uint32_t)sizeof(u32x4);
+        u32x4 x[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            x[i] = load_once<kStream>(reinterpret_cast<const char *>(a.r.in[i]) + row_bytes, off);
+        const u32x4 res = load_once<kStream>(reinterpret_cast<const char *>(a.r.residual) + row_bytes, off);
+        __builtin_amdgcn_sched_barrier(0);
+        F8 sum = widen(narrow(reduce_packs<N>(x)));  // the reduced value, in bf16
+        add_into(sum, widen(res));
+        const u32x4 ro = narrow(sum);
+        // read straight back by k_split_norm: an ordinary store, so that it can stay in the caches
+        store_pack(reinterpret_cast<char *>(a.r.residual_out) + row_bytes, off, ro);
+        const F8 y = widen(ro);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            ss = __builtin_fmaf(y.v[e], y.v[e], ss);
+    }
+    const float total = block_sum<false>(ss, slots);
+    if (threadIdx.x == 0)
+        a.partial[blockIdx.x] = total;
+}
+
+__global__ void __launch_bounds__(1024) k_split_norm(SplitArgs a)
+{
+    const uint32_t splits = (uint32_t)a.splits;
+    const uint32_t row = blockIdx.x / splits;
+    const uint32_t slice = blockIdx.x - row * splits;
+    const uint32_t packs = (uint32_t)a.r.packs;
+    const uint32_t p = slice * (uint32_t)a.slice_packs + threadIdx.x;
+    const size_t row_bytes = (size_t)row * packs * sizeof(u32x4);
+    const float *part = a.partial + (size_t)row * splits;
+    float total = part[0];
+    for (uint32_t i = 1; i < splits; ++i)
+        total = total + part[i];
+    const float rstd = rsqrt_f32(total * a.r.inv_hidden + a.r.eps);
+    if (threadIdx.x < (uint32_t)a.slice_packs && p < packs) {
+        const uint32_t off = p * (uint32_t)sizeof(u32x4);
+        const F8 y = widen(load_pack(reinterpret_cast<const char *>(a.r.residual_out) + row_bytes, off));
+        const F8 g = widen(load_pack(reinterpret_cast<const char *>(a.r.weight), off));
+        F8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            o.v[e] = (y.v[e] * rstd) * g.v[e];
+        store_stream(reinterpret_cast<char *>(a.r.out) + row_bytes, off, narrow(o));
+    }
+}
+
 // Stage 1 with LDS staging, one wave per input (the one-wave-per-rank design that the flat reduce
 // replaced: aiter PR #3817, Technical Details > 2stage > reduce-scatter), kept for comparison.
 // The page describes it only as staging through LDS with a workgroup barrier, one wave per rank;

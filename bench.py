@@ -29,6 +29,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_onestage_n8_m4096_h7168.t
 KERNEL_SOURCES = [os.path.join(ROOT, "all_reduce_residual_way_amd", "csrc", f)
                   for f in ("kernels.h", "bf16x8.h", "wave_sum.h", "fused_ar.hip")]
 DECODE_M = (1, 2, 4, 8, 16, 32)
+SPLIT = "split"  # Workload.call: the split-row entry point (slices chosen by the library)
 
 
 def log(msg):
@@ -139,12 +140,18 @@ class Workload:
                                   ro_t=torch.empty_like(t[-1]), out_t=torch.empty_like(t[-1])))
             self.sets[-1]["ro"] = self.sets[-1]["ro_t"].data_ptr()
             self.sets[-1]["out"] = self.sets[-1]["out_t"].data_ptr()
+        self.ws_bytes = fa.split_workspace_bytes(self.m, self.hidden, 0)
+        self.ws = torch.empty(max(self.ws_bytes, 4) // 4, dtype=torch.float32, device="cuda")
         torch.cuda.synchronize()
 
     def call(self, i, path, options=None, stream=None):
         s = self.sets[i % len(self.sets)]
         h = stream if stream is not None else self.torch.cuda.current_stream().cuda_stream
-        if path == self.fa.PATH_UNFUSED and options is None:
+        if path == SPLIT:
+            rc = self.lib.fused_ar_rmsnorm_split(s["arr"], self.n, s["res"], self.weight.data_ptr(),
+                                                 self.eps, self.m, self.hidden, s["ro"], s["out"], 0,
+                                                 self.ws.data_ptr(), self.ws_bytes, h)
+        elif path == self.fa.PATH_UNFUSED and options is None:
             rc = self.lib.fused_ar_unfused_rmsnorm(s["arr"], self.n, s["res"], self.weight.data_ptr(),
                                                    self.eps, self.m, self.hidden, s["ro"], s["out"], h)
         else:
@@ -414,6 +421,7 @@ def main():
 
     decode = None
     decode_designs = None
+    split_rows = None
     if not args.no_decode:
         decode, decode_designs = {}, {}
         for dm in DECODE_M:
@@ -436,6 +444,18 @@ def main():
             del dw
         if args.no_extra:
             decode_designs = None
+        else:
+            # wide rows at small m: one workgroup per row against rows cut into slices
+            split_rows = {}
+            for hid in (7168, 16384, 32768):
+                for dm in (1, 32):
+                    log(f"split rows hidden={hid} m={dm}")
+                    dw = Workload(torch, fa, synth.make_problem(8, dm, hid, seed=dm, name="decode"), 1)
+                    split_rows[f"hidden{hid}_m{dm}"] = {
+                        "onestage": round(dw.graph_latency_us(1), 3),
+                        "split": round(dw.graph_latency_us(SPLIT), 3),
+                        "slices": dw.ws_bytes // (4 * dm)}
+                    del dw
 
     cpu = None
     if not args.no_cpu:
@@ -484,6 +504,7 @@ def main():
         "paths": paths,
         "decode_us_per_call": decode,
         "decode_designs_us_per_call": decode_designs,
+        "split_rows_us_per_call": split_rows,
         "extra": extra,
         "parity_sampled_rows_ok": parity_ok,
         "device": props.name,

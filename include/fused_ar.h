@@ -33,6 +33,7 @@
 #ifndef FUSED_AR_H
 #define FUSED_AR_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -104,6 +105,37 @@ int fused_ar_rmsnorm(const fa_bf16 *const *inputs, int n, const fa_bf16 *residua
 int fused_ar_unfused_rmsnorm(const fa_bf16 *const *inputs, int n, const fa_bf16 *residual,
                              const fa_bf16 *weight, float eps, int m, int hidden,
                              fa_bf16 *residual_out, fa_bf16 *out, hipStream_t stream);
+
+/*
+ * fused_ar_rmsnorm_split - the one-stage result with every row cut into slices on separate
+ * workgroups, so that a few rows still spread over many CUs, in two kernels: the first reduces,
+ * adds the residual, writes residual_out and stores each slice's square-sum in `workspace`; the
+ * second sums a row's slice square-sums in slice order and normalises each slice. residual_out is
+ * bit-identical to fused_ar_rmsnorm's; out is deterministic and within the same 1-ulp band (its
+ * square-sum is grouped by slice). The pages do not describe this form: it applies the reasoning
+ * of aiter PR #3817 (Technical Details > 2stage > stage-1 launch config: more workgroups give small
+ * problems more CUs) to the one-stage row. Measured on MI355X (N = 8, calls in a HIP graph): faster
+ * than fused_ar_rmsnorm from hidden 16384 at m <= 32 (8.1 -> 4.7 us at hidden 32768, m = 1), slower
+ * at hidden <= 7168 and at m = 128, since its second launch costs about a kernel launch.
+ *
+ *   splits     slices per row, 1..64 (capped at hidden / 8, so that no slice is empty); 0 = one
+ *              slice per 256 packs of 8 elements. FUSED_AR_ERR_SHAPE if a slice would need more
+ *              than 1024 threads (one pack per thread); FUSED_AR_ERR_INVALID outside 0..64.
+ *   workspace  device buffer of at least fused_ar_split_workspace_bytes(m, hidden, splits) bytes,
+ *              16-byte aligned, overlapping no other buffer; its contents are overwritten and need
+ *              no initial value. Calls that share a workspace must be ordered (one stream).
+ *   Other arguments, conventions and errors as for fused_ar_rmsnorm with the one-stage path; the
+ *   workspace is checked after the other buffers (null or too small: FUSED_AR_ERR_INVALID,
+ *   misaligned: FUSED_AR_ERR_ALIGN, overlapping: FUSED_AR_ERR_ALIAS).
+ */
+int fused_ar_rmsnorm_split(const fa_bf16 *const *inputs, int n, const fa_bf16 *residual,
+                           const fa_bf16 *weight, float eps, int m, int hidden,
+                           fa_bf16 *residual_out, fa_bf16 *out, int splits, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* fused_ar_split_workspace_bytes - the workspace fused_ar_rmsnorm_split needs for these scalars
+ * (m * slices * 4 bytes); 0 when m == 0 or the scalars are invalid. */
+size_t fused_ar_split_workspace_bytes(int m, int hidden, int splits);
 
 /* Options of fused_ar_rmsnorm_ex: alternative kernel designs, for comparison and tuning. */
 enum {

@@ -220,6 +220,32 @@ static int gpu_checks(void)
     }
     HIP_OK(hipStreamDestroy(stream));
 
+    /* split rows: 3 slices of 22, 22 and 21 packs per row, the square-sums in a workspace */
+    {
+        const size_t ws_bytes = fused_ar_split_workspace_bytes(M, H, 3);
+        CHECK(ws_bytes == (size_t)M * 3 * sizeof(float));
+        void *d_ws;
+        HIP_OK(hipMalloc(&d_ws, ws_bytes));
+        HIP_OK(hipMemset(d_ro, 0xFF, plane * 2));
+        HIP_OK(hipMemset(d_out, 0xFF, plane * 2));
+        CHECK(fused_ar_rmsnorm_split(ins, N, d_res, d_w, eps, M, H, d_ro, d_out, 3, d_ws, ws_bytes - 4,
+                                     NULL) == FUSED_AR_ERR_INVALID);
+        CHECK(fused_ar_rmsnorm_split(ins, N, d_res, d_w, eps, M, H, d_ro, d_out, 3, d_ws, ws_bytes,
+                                     NULL) == FUSED_AR_OK);
+        HIP_OK(hipDeviceSynchronize());
+        HIP_OK(hipMemcpy(got_ro, d_ro, plane * 2, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(got_out, d_out, plane * 2, hipMemcpyDeviceToHost));
+        for (size_t j = 0; j < plane; ++j) {
+            const int d = ordinal(got_out[j]) - ordinal(want_out[j]);
+            if (got_ro[j] != want_ro[j] || d > 1 || d < -1) {
+                fprintf(stderr, "split rows: element %zu: residual_out %#06x (oracle %#06x), out %#06x "
+                        "(oracle %#06x)\n", j, got_ro[j], want_ro[j], got_out[j], want_out[j]);
+                return 1;
+            }
+        }
+        HIP_OK(hipFree(d_ws));
+    }
+
     /* the reduce alone, bit-exact against the oracle's */
     CHECK(oracle_reduce((const uint16_t *const *)h_in, N, (long long)plane, want_ro) == 0);
     HIP_OK(hipMemset(d_ro, 0xFF, plane * 2));
@@ -241,7 +267,7 @@ static int gpu_checks(void)
     HIP_OK(hipFree(d_ro));
     HIP_OK(hipFree(d_out));
     free(h_res); free(h_w); free(want_ro); free(want_out); free(got_ro); free(got_out);
-    printf("gpu checks passed: path 1, path 2 and unfused (eager and graph-captured) and the reduce match the oracle\n");
+    printf("gpu checks passed: path 1, path 2 and unfused (eager and graph-captured), split rows and the reduce match the oracle\n");
     return 0;
 }
 

@@ -284,3 +284,49 @@ def test_automatic_load_policy():
         assert streaming(n, m_max, hidden, fa.PATH_UNFUSED) == [0, 0, 0]
     assert streaming(8, 4096, 7168, 1, fa.Options(0, 0, 0, 0, fa.LOAD_CACHED)) == [0]
     assert streaming(8, 8, 7168, 1, fa.Options(0, 0, 0, 0, fa.LOAD_STREAM)) == [1]
+
+
+def split_call(n=4, m=8, hidden=4096, eps=1e-6, inputs=None, residual=None, weight=None,
+               residual_out=None, out=None, splits=0, workspace=None, workspace_bytes=None):
+    ins = inputs if inputs is not None else [addr(i) for i in range(n)]
+    need = fa.split_workspace_bytes(m, hidden, splits)
+    return fa.fused_ar_rmsnorm_split_ptrs(
+        ins, addr(10) if residual is None else residual, addr(11) if weight is None else weight,
+        eps, m, hidden, addr(12) if residual_out is None else residual_out,
+        addr(13) if out is None else out, splits, addr(14) if workspace is None else workspace,
+        need if workspace_bytes is None else workspace_bytes, 0)
+
+
+@pytest.mark.parametrize("kwargs,code", [c for c in BAD_CALLS if "path" not in c[0]] + [
+    (dict(splits=65), fa.ERR_INVALID),
+    (dict(splits=-1), fa.ERR_INVALID),
+    (dict(hidden=16384, splits=1), fa.ERR_SHAPE),             # 2048 packs in one slice
+    (dict(workspace=0), fa.ERR_INVALID),
+    (dict(workspace_bytes=8 * 2 * 4 - 4), fa.ERR_INVALID),   # one float short (2 slices of 256)
+    (dict(workspace=addr(14) + 4), fa.ERR_ALIGN),
+    (dict(workspace=addr(13) + 64), fa.ERR_ALIAS),           # inside out
+    (dict(workspace=addr(2)), fa.ERR_ALIAS),                 # inside an input
+    (dict(workspace=addr(11)), fa.ERR_ALIAS),                # the weight
+    (dict(workspace=addr(10) + 4096), fa.ERR_ALIAS),         # inside the residual
+    (dict(workspace=addr(12)), fa.ERR_ALIAS),                # residual_out
+])
+def test_split_rejected_before_launch(kwargs, code):
+    kwargs = dict(kwargs)
+    kwargs.setdefault("n", len(kwargs["inputs"]) if "inputs" in kwargs else 4)
+    assert split_call(**kwargs) == code
+
+
+def test_split_workspace_and_slices():
+    # one slice per 256 packs unless given; never more slices than packs; at most 64
+    assert fa.split_workspace_bytes(1, 7168) == 4 * 4
+    assert fa.split_workspace_bytes(5, 32768) == 5 * 16 * 4
+    assert fa.split_workspace_bytes(3, 520) == 3 * 1 * 4
+    assert fa.split_workspace_bytes(2, 7168, 7) == 2 * 7 * 4
+    assert fa.split_workspace_bytes(1, 8, 3) == 4          # one pack: one slice
+    assert fa.split_workspace_bytes(1, 7168, 64) == 64 * 4
+    assert fa.split_workspace_bytes(1, 7168, 65) == 0
+    assert fa.split_workspace_bytes(0, 7168) == 0
+    assert fa.split_workspace_bytes(1, 16384, 1) == 0      # a slice would need 2048 threads
+    assert fa.split_workspace_bytes(1, 12) == 0            # hidden not a multiple of 8
+    # m == 0: success before any pointer is looked at
+    assert fa.fused_ar_rmsnorm_split_ptrs([0], 0, 0, 1e-6, 0, 4096, 0, 0, 0, 0, 0, 0) == fa.OK

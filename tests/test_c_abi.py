@@ -39,7 +39,7 @@ def test_c_client_cpu_entry_points(program):
 
 @pytest.mark.gpu
 def test_c_client_on_gpu(program):
-    print("[gpu case] C client, n=5 m=7 hidden=520, paths 1, 2, unfused, graph capture, reduce", flush=True)
+    print("[gpu case] C client, n=5 m=7 hidden=520, paths 1, 2, unfused, graph capture, split rows, reduce", flush=True)
     r = subprocess.run([program, "gpu"], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
     assert "gpu checks passed" in r.stdout

@@ -478,3 +478,77 @@ def test_randomized_shapes_paths_and_options():
         torch.cuda.synchronize()
         want_ro, want_out = oracle_rows(p)
         assert_parity(name, host(ro), host(out), want_ro, want_out)
+
+
+# ------------------------------------------------------------------------- split rows
+
+def run_split(p, splits, in_place=False, workspace=None):
+    ins = [dev(x) for x in p.inputs]
+    res = dev(p.residual)
+    w = dev(p.weight)
+    ro = res if in_place else torch.empty_like(res)
+    out = torch.empty_like(res)
+    fa.fused_ar_rmsnorm_split(ins, res, w, p.eps, splits=splits, workspace=workspace,
+                              residual_out=ro, out=out)
+    torch.cuda.synchronize()
+    return host(ro), host(out)
+
+
+@pytest.mark.parametrize("n,m,hidden,splits", [
+    (8, 1, 7168, 0),      # 4 slices of 224 packs
+    (8, 1, 7168, 1),      # one slice: the one-stage row
+    (8, 3, 7168, 4),
+    (8, 32, 7168, 7),     # 128 packs per slice, the last one short
+    (4, 8, 4096, 0),
+    (8, 2, 32768, 0),     # 16 slices of 256 packs
+    (8, 1, 32768, 4),     # 4 slices of 1024 packs: full 1024-thread workgroups
+    (5, 17, 520, 3),      # 65 packs: slices of 22, 22, 21
+    (1, 5, 2880, 0),
+    (2, 4, 8, 3),         # one pack per row: capped at one slice
+    (8, 9, 2880, 64),     # 360 packs in slices of 6: the last four slices are empty
+])
+def test_split_rows_match_the_oracle(n, m, hidden, splits):
+    p = synth.make_problem(n, m, hidden, seed=7000 + m + splits, name="split")
+    announce(f"split rows n={n} m={m} hidden={hidden} splits={splits}")
+    ro, out = run_split(p, splits)
+    want_ro, want_out = oracle_rows(p)
+    assert_parity(f"split n={n} m={m} hidden={hidden} splits={splits}", ro, out, want_ro, want_out)
+    one_ro, _ = run_gpu(p, 1)
+    assert np.array_equal(ro, one_ro)  # the same residual_out bits as the one-stage path
+    again = run_split(p, splits)
+    assert np.array_equal(ro, again[0]) and np.array_equal(out, again[1])  # deterministic
+
+
+def test_split_rows_stress_in_place_and_reused_workspace():
+    """Zero rows, +-3e4 rows and ties, in place (residual_out == residual), one workspace reused
+    by calls of different sizes."""
+    ws = torch.empty(64 * 64, dtype=torch.float32, device="cuda")
+    for m, splits in ((40, 0), (7, 5), (64, 3)):
+        p = synth.make_problem(8, m, 2880, seed=7100 + m, dist="stress", name="split stress")
+        announce(f"split rows stress in place m={m} splits={splits}")
+        ro, out = run_split(p, splits, in_place=True, workspace=ws)
+        want_ro, want_out = oracle_rows(p)
+        assert_parity(f"split stress m={m}", ro, out, want_ro, want_out)
+
+
+def test_split_rows_graph_replay():
+    p = synth.make_problem(8, 4, 7168, seed=7200)
+    ins = [dev(x) for x in p.inputs]
+    res, w = dev(p.residual), dev(p.weight)
+    ro_e, out_e = fa.fused_ar_rmsnorm_split(ins, res, w, p.eps)
+    ws = torch.empty(fa.split_workspace_bytes(4, 7168) // 4, dtype=torch.float32, device="cuda")
+    ro, out = torch.empty_like(res), torch.empty_like(res)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(10):
+            fa.fused_ar_rmsnorm_split(ins, res, w, p.eps, workspace=ws, residual_out=ro, out=out)
+    for replay in range(3):
+        announce(f"split rows graph replay {replay}")
+        ro.zero_()
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ro.view(torch.int16), ro_e.view(torch.int16)), replay
+        assert torch.equal(out.view(torch.int16), out_e.view(torch.int16)), replay
