@@ -113,6 +113,29 @@ static int cpu_checks(void)
     /* automatic load policy: ordinary loads up to 128 MiB read per call, streaming above */
     CHECK(fused_ar_describe_launch(8, 1040, 7168, 1, &plan) == FUSED_AR_OK && plan.launch[0].streaming == 0);
     CHECK(fused_ar_describe_launch(8, 1041, 7168, 1, &plan) == FUSED_AR_OK && plan.launch[0].streaming == 1);
+    /* split rows: workspace size, scalar and buffer checks (all rejected before any launch) */
+    CHECK(fused_ar_split_workspace_bytes(3, 7168, 0) == 3u * 4u * sizeof(float));
+    CHECK(fused_ar_split_workspace_bytes(2147483647, 32768, 64) == (size_t)2147483647 * 64u * 4u);
+    CHECK(fused_ar_split_workspace_bytes(-1, 7168, 0) == 0 && fused_ar_split_workspace_bytes(1, 7168, 65) == 0);
+    CHECK(fused_ar_split_workspace_bytes(1, 16384, 1) == 0 && fused_ar_split_workspace_bytes(1, 4100, 0) == 0);
+    {
+        void *ws = (void *)fake(7);
+        const size_t need = fused_ar_split_workspace_bytes(8, 4096, 0);
+        CHECK(fused_ar_rmsnorm_split(ins, 3, fake(3), fake(4), 1e-6f, 8, 4096, (fa_bf16 *)fake(5),
+                                     (fa_bf16 *)fake(6), 0, NULL, need, NULL) == FUSED_AR_ERR_INVALID);
+        CHECK(fused_ar_rmsnorm_split(ins, 3, fake(3), fake(4), 1e-6f, 8, 4096, (fa_bf16 *)fake(5),
+                                     (fa_bf16 *)fake(6), 0, ws, need - 1, NULL) == FUSED_AR_ERR_INVALID);
+        CHECK(fused_ar_rmsnorm_split(ins, 3, fake(3), fake(4), 1e-6f, 8, 4096, (fa_bf16 *)fake(5),
+                                     (fa_bf16 *)fake(6), 0, (char *)ws + 8, need, NULL) == FUSED_AR_ERR_ALIGN);
+        CHECK(fused_ar_rmsnorm_split(ins, 3, fake(3), fake(4), 1e-6f, 8, 4096, (fa_bf16 *)fake(5),
+                                     (fa_bf16 *)fake(6), 0, (void *)fake(6), need, NULL) == FUSED_AR_ERR_ALIAS);
+        CHECK(fused_ar_rmsnorm_split(ins, 3, fake(3), fake(4), 1e-6f, 8, 4096, (fa_bf16 *)fake(5),
+                                     (fa_bf16 *)fake(6), 99, ws, need, NULL) == FUSED_AR_ERR_INVALID);
+        CHECK(fused_ar_rmsnorm_split(ins, 3, fake(3), fake(4), 1e-6f, 8, 16384, (fa_bf16 *)fake(5),
+                                     (fa_bf16 *)fake(6), 1, ws, need, NULL) == FUSED_AR_ERR_SHAPE);
+        CHECK(fused_ar_rmsnorm_split(NULL, 3, NULL, NULL, 1e-6f, 0, 4096, NULL, NULL, 0, NULL, 0, NULL) ==
+              FUSED_AR_OK); /* m == 0 */
+    }
     printf("cpu checks passed\n");
     return 0;
 }
