@@ -397,6 +397,12 @@ def main():
     for p in (1, 2):
         if str(p) not in paths:
             paths[str(p)] = entry(p, work.time_ms(p, short, args.warmup))
+    if work.ws_bytes > 0:  # the split-row form (slices chosen by the library), same problem
+        sms = work.time_ms(SPLIT, short, args.warmup)
+        paths[SPLIT] = {"us_per_call": round(sms * 1e3, 3),
+                        "gbs_algorithmic": round(bytes_alg / (sms * 1e-3) / 1e9, 1),
+                        "kernels": ["split_reduce", "split_norm"],
+                        "slices": work.ws_bytes // (4 * m)}
 
     extra = None
     if not args.no_extra:
