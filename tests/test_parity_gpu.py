@@ -450,11 +450,11 @@ def test_forced_packs_per_thread(ppt):
 # ------------------------------------------------------------------------- randomized sweep
 
 def test_randomized_shapes_paths_and_options():
-    """40 seeded random cases: n in 1..8, m in 1..300, hidden any multiple of 8 up to 9600, every
+    """80 seeded random cases: n in 1..8, m in 1..300, hidden any multiple of 8 up to 9600, every
     path (auto, one-stage, two-stage, unfused), random design options and eps, normal or stress
     values; each compared whole with the oracle."""
     rng = np.random.default_rng(2024)
-    for case in range(40):
+    for case in range(80):
         n = int(rng.integers(1, 9))
         m = int(rng.integers(1, 301))
         hidden = 8 * int(rng.integers(1, 1201))
@@ -552,3 +552,25 @@ def test_split_rows_graph_replay():
         torch.cuda.synchronize()
         assert torch.equal(ro.view(torch.int16), ro_e.view(torch.int16)), replay
         assert torch.equal(out.view(torch.int16), out_e.view(torch.int16)), replay
+
+
+def test_split_rows_randomized():
+    """30 seeded random split-row cases: n in 1..8, m in 1..96, hidden any multiple of 8 up to
+    32768, slices 0 (automatic) or 1..64 where a slice fits 1024 threads, eps and value mix at
+    random; each compared whole with the oracle."""
+    rng = np.random.default_rng(2025)
+    for case in range(30):
+        n = int(rng.integers(1, 9))
+        m = int(rng.integers(1, 97))
+        hidden = 8 * int(rng.integers(1, 4097))
+        splits = int(rng.choice([0, int(rng.integers(1, 65))]))
+        if fa.split_workspace_bytes(m, hidden, splits) == 0:
+            splits = 0  # too few slices for one pack per thread: let the library choose
+        eps = float(rng.choice([1e-6, 1e-5, 0.1]))
+        dist = "stress" if rng.random() < 0.3 else "normal"
+        p = synth.make_problem(n, m, hidden, seed=6000 + case, eps=eps, dist=dist, name="random split")
+        name = f"random split case {case}: n={n} m={m} hidden={hidden} splits={splits} eps={eps} {dist}"
+        announce(name)
+        ro, out = run_split(p, splits)
+        want_ro, want_out = oracle_rows(p)
+        assert_parity(name, ro, out, want_ro, want_out)
