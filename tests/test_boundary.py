@@ -212,6 +212,11 @@ def test_binding_rejects_bad_tensors_without_a_gpu():
         fa.fused_ar_rmsnorm([x.float()], x, torch.zeros(16, dtype=torch.bfloat16))
     with pytest.raises(ValueError):
         fa.fused_ar_rmsnorm([], x, x[0])
+    for call in (fa.fused_ar_unfused_rmsnorm, fa.fused_ar_rmsnorm_split):
+        with pytest.raises(ValueError):
+            call([x], x, torch.zeros(16, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        fa.fused_ar_reduce([x])
 
 
 def test_options_struct_matches_header():
