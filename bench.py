@@ -397,6 +397,9 @@ def main():
     for p in (1, 2):
         if str(p) not in paths:
             paths[str(p)] = entry(p, work.time_ms(p, short, args.warmup))
+    moved_two_stage = 2 * (n + 5) * m * hidden + 2 * hidden  # + the scratch written and read back
+    paths["2"]["moved_bytes"] = moved_two_stage
+    paths["2"]["gbs_moved"] = round(moved_two_stage / (paths["2"]["us_per_call"] * 1e-6) / 1e9, 1)
     if work.ws_bytes > 0:  # the split-row form (slices chosen by the library), same problem
         sms = work.time_ms(SPLIT, short, args.warmup)
         paths[SPLIT] = {"us_per_call": round(sms * 1e3, 3),
