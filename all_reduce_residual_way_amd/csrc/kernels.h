@@ -7,6 +7,11 @@
 //   k_flat_reduce<N>   stage 1 of the two-stage path: one thread per pack, N-way fp32 reduce,
 //                      one bf16 store, no LDS and no workgroup barrier (Technical Details >
 //                      2stage > reduce-scatter).
+//   k_split_reduce<N>, k_split_norm
+//                      split rows: the one-stage result with each row cut into slices on separate
+//                      workgroups, the second kernel combining the slices' square-sums.
+//   k_stage1_lds<N>    the LDS-staged, one-wave-per-input stage 1 that the flat reduce replaced,
+//                      kept for comparison.
 //
 // Both read and write 16-byte packs of eight bf16; a row of `hidden` elements is hidden / 8 packs
 // and consecutive lanes touch consecutive packs, so every wave access is 1 KiB contiguous.
