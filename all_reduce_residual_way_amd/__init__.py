@@ -39,7 +39,7 @@ _VP = ctypes.c_void_p
 class _KernelLaunch(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 32), ("grid", ctypes.c_uint), ("block", ctypes.c_uint),
                 ("per_thread", ctypes.c_uint), ("launches", ctypes.c_uint),
-                ("streaming", ctypes.c_uint)]
+                ("streaming", ctypes.c_uint), ("lds_bytes", ctypes.c_uint)]
 
 
 class _LaunchPlan(ctypes.Structure):
@@ -134,7 +134,8 @@ def describe_launch(n, m, hidden, path=PATH_AUTO, options=None):
         "kernels": [
             {"name": plan.launch[i].name.decode(), "grid": plan.launch[i].grid,
              "block": plan.launch[i].block, "per_thread": plan.launch[i].per_thread,
-             "launches": plan.launch[i].launches, "streaming": plan.launch[i].streaming}
+             "launches": plan.launch[i].launches, "streaming": plan.launch[i].streaming,
+             "lds_bytes": plan.launch[i].lds_bytes}
             for i in range(plan.kernels)
         ],
     }

@@ -310,9 +310,21 @@ struct Step {
     const void *kernel;
     const char *name;
     unsigned grid, block, per_thread, launches;
-    int n;        // inputs this step reads
-    bool stream;  // non-temporal loads
+    int n;             // inputs this step reads
+    bool stream;       // non-temporal loads
+    unsigned lds = 0;  // dynamic LDS reserved per workgroup (bytes), to cap workgroups per CU
 };
+
+// Rows in flight when streaming from HBM. With more than about two row workgroups per CU (small
+// rows let up to five reside) the reads of ~1000 rows interleave across the planes and HBM serves
+// them less efficiently: capping the row kernel at two resident workgroups per CU (~512 rows in
+// flight) measured +4.1 points of peak at hidden 2880, +3.0 at 4096, +1.5 at 5120 (N = 8, 24576 /
+// 16384 / 13107 rows), no change at 7168 and 8192, where two is already the limit. The cap is a
+// reservation of LDS the kernel does not use: 64 KiB of the CU's 160 KiB admits two workgroups,
+// not three. It applies only to calls that stream (cache-resident calls lose by it: -3.9 points at
+// hidden 2880, m = 1000, warm) and have more than kTwoPackMaxM rows, so that the rows of the
+// two-pack band stay resident in one round.
+constexpr unsigned kRowCapLds = 64u * 1024u;
 
 struct Plan {
     int path;  // FUSED_AR_PATH_ONESTAGE, FUSED_AR_PATH_TWOSTAGE or kPathUnfusedPlan
@@ -349,6 +361,8 @@ int make_plan(int n, int m, int hidden, int path, const Options &o, Plan *plan)
     Step rows{nullptr, "", static_cast<unsigned>(m < kRowsPerLaunch ? m : kRowsPerLaunch),
               static_cast<unsigned>(threads), static_cast<unsigned>(ppt),
               static_cast<unsigned>(launches), n, stream};
+    if (stream && m > kTwoPackMaxM)
+        rows.lds = kRowCapLds;
     if (path == FUSED_AR_PATH_ONESTAGE) {
         rows.kernel = row_kernel(n, ppt, o.bpermute, true, stream);
         rows.name = "onestage";
@@ -381,10 +395,11 @@ int make_plan(int n, int m, int hidden, int path, const Options &o, Plan *plan)
     return FUSED_AR_OK;
 }
 
-int launch(const void *kernel, unsigned grid, unsigned block, void *args, hipStream_t stream)
+int launch(const void *kernel, unsigned grid, unsigned block, void *args, hipStream_t stream,
+           unsigned lds = 0)
 {
     void *params[] = {args};
-    const hipError_t e = hipLaunchKernel(kernel, dim3(grid), dim3(block), params, 0, stream);
+    const hipError_t e = hipLaunchKernel(kernel, dim3(grid), dim3(block), params, lds, stream);
     return e == hipSuccess ? FUSED_AR_OK : static_cast<int>(e);
 }
 
@@ -401,7 +416,7 @@ int run_rows(const Step &s, const RowArgs &args, int m, int packs, hipStream_t s
         a.residual += skip;
         a.residual_out += skip;
         a.out += skip;
-        const int rc = launch(s.kernel, static_cast<unsigned>(rows), s.block, &a, stream);
+        const int rc = launch(s.kernel, static_cast<unsigned>(rows), s.block, &a, stream, s.lds);
         if (rc != FUSED_AR_OK)
             return rc;
     }
@@ -685,6 +700,7 @@ extern "C" int fused_ar_describe_launch_ex(int n, int m, int hidden, int path,
         k.per_thread = p.step[i].per_thread;
         k.launches = p.step[i].launches;
         k.streaming = p.step[i].stream ? 1u : 0u;
+        k.lds_bytes = p.step[i].lds;
     }
     return FUSED_AR_OK;
 }

@@ -225,6 +225,8 @@ typedef struct {
     unsigned launches;    /* launches of this kernel per call: rows come in launches of at most
                              2^20 workgroups, flat kernels' packs in launches of at most 2^30 */
     unsigned streaming;   /* 1: non-temporal loads of the inputs; 0: ordinary loads */
+    unsigned lds_bytes;   /* LDS reserved per workgroup beyond the kernel's own, to cap the
+                             workgroups resident per CU (row kernels of long streaming calls) */
 } fused_ar_kernel_launch;
 
 typedef struct {

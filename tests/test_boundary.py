@@ -335,3 +335,28 @@ def test_split_workspace_and_slices():
     assert fa.split_workspace_bytes(1, 12) == 0            # hidden not a multiple of 8
     # m == 0: success before any pointer is looked at
     assert fa.fused_ar_rmsnorm_split_ptrs([0], 0, 0, 1e-6, 0, 4096, 0, 0, 0, 0, 0, 0) == fa.OK
+
+
+def test_launch_plan_struct_matches_header():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    body = re.search(r"typedef struct \{(.*?)\} fused_ar_kernel_launch;", text, re.S).group(1)
+    fields = re.findall(r"(?:unsigned|char) (\w+)", body)
+    assert fields == [name for name, _ in fa._KernelLaunch._fields_]
+
+
+def test_row_workgroups_capped_on_long_streaming_calls():
+    # LDS reserved on the row kernel (two workgroups per CU) only when the call streams from HBM
+    # and has more rows than the two-pack band; never on the flat kernels
+    def lds(n, m, hidden, path=1, opt=None):
+        return [k["lds_bytes"] for k in fa.describe_launch(n, m, hidden, path, opt)["kernels"]]
+    assert lds(8, 4096, 7168) == [64 * 1024]
+    assert lds(8, 24576, 2880) == [64 * 1024]
+    assert lds(8, 4096, 7168, 2) == [0, 64 * 1024]
+    assert lds(8, 4096, 7168, fa.PATH_UNFUSED) == [0, 0, 64 * 1024]
+    assert lds(8, 1000, 2880) == [0]                      # reads under 128 MiB: cached, no cap
+    assert lds(8, 1024, 8192) == [0]                      # streams, but within the two-pack band
+    assert lds(8, 1025, 8192) == [64 * 1024]
+    assert lds(8, 32, 7168) == [0]
+    assert lds(8, 4096, 7168, 1, fa.Options(0, 0, 0, 0, fa.LOAD_CACHED)) == [0]
