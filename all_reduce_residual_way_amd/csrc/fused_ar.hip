@@ -162,21 +162,41 @@ int read_options(const fused_ar_options *o, Options *out)
 }
 
 // Packs per thread and threads per workgroup of the row kernel for m rows of `packs` packs.
-// One pack per thread where the row fits in 1024 threads: each thread issues all its loads at
-// once and a row costs one memory round trip. Exception, from measurements on MI355X (N = 4 and
-// 8, hidden 4096-8192): for 256 < m <= 1024 rows wider than 512 packs, two packs per thread
-// (half-size workgroups, twice as many resident per CU) are up to 7 % faster; elsewhere one pack
-// per thread is as fast or up to 4 % faster. Packs per thread grow (1, 2, 4) until the row fits
-// in 1024 threads; the thread count is rounded up to whole waves.
-// FUSED_AR_MAX_HIDDEN = 4 * 1024 * 8 elements.
+// Calls that read from the caches, or that have few rows: one pack per thread where the row fits
+// in 1024 threads, so that each thread issues all its loads at once and a row costs one memory
+// round trip; except that for 256 < m <= 1024 rows wider than 512 packs two packs per thread
+// (half-size workgroups, twice as many resident per CU) are up to 7 % faster (measured on MI355X,
+// N = 4 and 8, hidden 4096-8192).
+// Long calls that stream from HBM (`capped`: at most two row workgroups per CU, see kRowCapLds)
+// go best with fewer threads per row, its packs taken in turn: two packs per thread for rows of
+// 512-1024 packs and four above, one below (N = 8, cold, % of peak with one / two / four packs
+// per thread: hidden 2880 79.7 / 77.4 / 73.7, 4096 77.2 / 80.0 / 76.3, 6144 73.7 / 75.7 / 77.2,
+// 7168 75.8 / 76.4 / 75.6, 8192 75.8 / 77.4 / 76.0, 16384 - / 73.3 / 73.9).
+// Packs per thread grow (1, 2, 4) until the row fits in 1024 threads; the thread count is
+// rounded up to whole waves. FUSED_AR_MAX_HIDDEN = 4 * 1024 * 8 elements.
 constexpr int kTwoPackMinM = 257;
 constexpr int kTwoPackMaxM = 1024;
 
-int row_geometry(int packs, int m, int forced_ppt, int *ppt, int *threads)
+// Row workgroups resident per CU on long streaming calls. Small rows let up to five row
+// workgroups reside per CU, about 1000 rows in flight, and HBM then serves the interleaved reads
+// less well: capping the row kernel at two resident workgroups per CU (about 512 rows in flight)
+// measured +4.0 points of peak at hidden 2880, +3.5 at 4096 and +1.3 at 5120 (N = 8, one pack per
+// thread). The cap is a reservation of LDS the kernel does not use: 64 KiB of the CU's 160 KiB
+// admits two workgroups, not three. It applies to calls that stream (cache-resident calls lose
+// by it: -3.9 points at hidden 2880, m = 1000, warm) and have more than kTwoPackMaxM rows, so that
+// the rows of the two-pack band stay resident in one round.
+constexpr unsigned kRowCapLds = 64u * 1024u;
+
+bool rows_capped(bool stream, int m) { return stream && m > kTwoPackMaxM; }
+
+int row_geometry(int packs, int m, int forced_ppt, bool capped, int *ppt, int *threads)
 {
     int k = forced_ppt;
     if (k == 0) {
-        k = (m >= kTwoPackMinM && m <= kTwoPackMaxM && packs > 512) ? 2 : 1;
+        if (capped)
+            k = packs > 1024 ? 4 : (packs >= 512 ? 2 : 1);
+        else
+            k = (m >= kTwoPackMinM && m <= kTwoPackMaxM && packs > 512) ? 2 : 1;
         while (k < 4 && (packs + k - 1) / k > kMaxBlock)
             k *= 2;
     } else if ((packs + k - 1) / k > kMaxBlock) {
@@ -315,16 +335,6 @@ struct Step {
     unsigned lds = 0;  // dynamic LDS reserved per workgroup (bytes), to cap workgroups per CU
 };
 
-// Rows in flight when streaming from HBM. With more than about two row workgroups per CU (small
-// rows let up to five reside) the reads of ~1000 rows interleave across the planes and HBM serves
-// them less efficiently: capping the row kernel at two resident workgroups per CU (~512 rows in
-// flight) measured +4.1 points of peak at hidden 2880, +3.0 at 4096, +1.5 at 5120 (N = 8, 24576 /
-// 16384 / 13107 rows), no change at 7168 and 8192, where two is already the limit. The cap is a
-// reservation of LDS the kernel does not use: 64 KiB of the CU's 160 KiB admits two workgroups,
-// not three. It applies only to calls that stream (cache-resident calls lose by it: -3.9 points at
-// hidden 2880, m = 1000, warm) and have more than kTwoPackMaxM rows, so that the rows of the
-// two-pack band stay resident in one round.
-constexpr unsigned kRowCapLds = 64u * 1024u;
 
 struct Plan {
     int path;  // FUSED_AR_PATH_ONESTAGE, FUSED_AR_PATH_TWOSTAGE or kPathUnfusedPlan
@@ -351,17 +361,18 @@ int make_plan(int n, int m, int hidden, int path, const Options &o, Plan *plan)
     if (m == 0)
         return FUSED_AR_OK;
     const int packs = hidden / kPackElems;
+    const bool stream = use_stream(o, n, m, hidden);
+    const bool capped = rows_capped(stream, m);
     int ppt, threads;
-    const int rc = row_geometry(packs, m, o.ppt, &ppt, &threads);
+    const int rc = row_geometry(packs, m, o.ppt, capped, &ppt, &threads);
     if (rc != FUSED_AR_OK)
         return rc;
     const size_t total = (size_t)m * (size_t)packs;
-    const bool stream = use_stream(o, n, m, hidden);
     const int64_t launches = ((int64_t)m + kRowsPerLaunch - 1) / kRowsPerLaunch;
     Step rows{nullptr, "", static_cast<unsigned>(m < kRowsPerLaunch ? m : kRowsPerLaunch),
               static_cast<unsigned>(threads), static_cast<unsigned>(ppt),
               static_cast<unsigned>(launches), n, stream};
-    if (stream && m > kTwoPackMaxM)
+    if (capped)
         rows.lds = kRowCapLds;
     if (path == FUSED_AR_PATH_ONESTAGE) {
         rows.kernel = row_kernel(n, ppt, o.bpermute, true, stream);

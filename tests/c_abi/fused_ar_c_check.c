@@ -40,7 +40,8 @@ static int cpu_checks(void)
     fused_ar_launch_plan plan;
     CHECK(fused_ar_describe_launch(8, 4096, 7168, FUSED_AR_PATH_ONESTAGE, &plan) == FUSED_AR_OK);
     CHECK(plan.kernels == 1 && strcmp(plan.launch[0].name, "onestage") == 0);
-    CHECK(plan.launch[0].grid == 4096 && plan.launch[0].block == 896);
+    CHECK(plan.launch[0].grid == 4096 && plan.launch[0].block == 448 && plan.launch[0].per_thread == 2 &&
+          plan.launch[0].lds_bytes == 64u * 1024u); /* a long streaming call: two packs per thread */
     CHECK(fused_ar_describe_launch(8, 4096, 7168, FUSED_AR_PATH_UNFUSED, &plan) == FUSED_AR_OK);
     CHECK(plan.kernels == 3 && strcmp(plan.launch[2].name, "rmsnorm") == 0);
     fused_ar_options opt = {FUSED_AR_WAVE_BPERMUTE, FUSED_AR_STAGE1_LDS, 0, 0, FUSED_AR_LOAD_AUTO};

@@ -170,8 +170,9 @@ def test_launch_geometry_covers_each_row(hidden):
 
 
 def test_launch_geometry_by_row_count():
-    # one pack per thread, except two for 256 < m <= 1024 on rows wider than 512 packs; rows come
-    # in launches of at most 2^20 workgroups
+    # calls from the caches: one pack per thread, except two for 256 < m <= 1024 on rows wider
+    # than 512 packs; long streaming calls (two workgroups per CU): one pack per thread below 512
+    # packs, two up to 1024, four above; rows come in launches of at most 2^20 workgroups
     k = fa.describe_launch(8, 256, 7168, 1)["kernels"][0]
     assert (k["per_thread"], k["block"], k["launches"]) == (1, 896, 1)
     k = fa.describe_launch(8, 257, 7168, 1)["kernels"][0]
@@ -181,9 +182,16 @@ def test_launch_geometry_by_row_count():
     k = fa.describe_launch(8, 1025, 7168, 1)["kernels"][0]
     assert (k["per_thread"], k["block"]) == (1, 896)
     k = fa.describe_launch(8, 4096, 16384, 1)["kernels"][0]
-    assert (k["per_thread"], k["block"]) == (2, 1024)
+    assert (k["per_thread"], k["block"], k["lds_bytes"]) == (4, 512, 64 * 1024)
     k = fa.describe_launch(8, 4096, 2880, 1)["kernels"][0]
-    assert (k["per_thread"], k["block"]) == (1, 384)
+    assert (k["per_thread"], k["block"], k["lds_bytes"]) == (1, 384, 64 * 1024)
+    for m, hidden, want in ((4096, 7168, (2, 448)), (2048, 7168, (2, 448)), (4096, 4096, (2, 256)),
+                            (8192, 8192, (2, 512)), (4096, 3584, (1, 448)), (4096, 32768, (4, 1024))):
+        k = fa.describe_launch(8, m, hidden, 1)["kernels"][0]
+        assert (k["per_thread"], k["block"]) == want, (m, hidden)
+    # the same call forced to ordinary loads reads as a cached call: not capped, one pack
+    k = fa.describe_launch(8, 4096, 7168, 1, fa.Options(0, 0, 0, 0, fa.LOAD_CACHED))["kernels"][0]
+    assert (k["per_thread"], k["block"], k["lds_bytes"]) == (1, 896, 0)
     k = fa.describe_launch(2, (1 << 20) + 3, 8, 2)["kernels"][1]
     assert (k["grid"], k["launches"]) == (1 << 20, 2)
 
