@@ -574,3 +574,37 @@ def test_split_rows_randomized():
         ro, out = run_split(p, splits)
         want_ro, want_out = oracle_rows(p)
         assert_parity(name, ro, out, want_ro, want_out)
+
+
+def test_long_streaming_calls_randomized():
+    """8 seeded random calls long enough to stream from HBM (over 128 MiB read, over 1024 rows),
+    where the row kernels are capped at two workgroups per CU and take 1, 2 or 4 packs per thread
+    by row width: sampled rows against the oracle, and paths 1 and 2 and the unfused sequence
+    bit-identical to each other."""
+    rng = np.random.default_rng(2026)
+    for case in range(8):
+        n = int(rng.integers(2, 9))
+        hidden = 8 * int(rng.integers(200, 4097))
+        m = (128 << 20) // (2 * (n + 1) * hidden) + int(rng.integers(1, 600))
+        m = max(m, 1025)
+        plan = fa.describe_launch(n, m, hidden, 1)["kernels"][0]
+        assert plan["streaming"] == 1 and plan["lds_bytes"] > 0, plan
+        p = synth.make_problem(n, m, hidden, seed=8000 + case, name="long streaming")
+        name = (f"long streaming case {case}: n={n} m={m} hidden={hidden} "
+                f"packs/thread={plan['per_thread']} block={plan['block']}")
+        announce(name)
+        ins = [dev(x) for x in p.inputs]
+        res, w = dev(p.residual), dev(p.weight)
+        got = {}
+        for path in (1, 2, fa.PATH_UNFUSED):
+            ro, out = fa.fused_ar_rmsnorm(ins, res, w, p.eps, path=path)
+            torch.cuda.synchronize()
+            got[path] = (ro.view(torch.int16), out.view(torch.int16))
+        for path in (2, fa.PATH_UNFUSED):
+            assert torch.equal(got[path][0], got[1][0]) and torch.equal(got[path][1], got[1][1]), path
+        rows = sample_rows(p, count=24, seed=case)
+        want_ro, want_out = oracle_rows(p, rows)
+        assert_parity(name, host(got[1][0].view(torch.bfloat16))[rows],
+                      host(got[1][1].view(torch.bfloat16))[rows], want_ro, want_out)
+        del ins, res, got
+        torch.cuda.empty_cache()
