@@ -165,15 +165,18 @@ typedef struct {
     int packs_per_thread;  /* row kernels: 0 = automatic, else 1, 2 or 4 (FUSED_AR_ERR_SHAPE if the
                               row then needs more than 1024 threads) */
     int load_policy;       /* FUSED_AR_LOAD_AUTO, FUSED_AR_LOAD_CACHED or FUSED_AR_LOAD_STREAM: how
-                              the inputs and the residual are loaded (results are the same bits) */
+                              the inputs and the residual are loaded; streaming calls of more than
+                              1024 rows also cap the row workgroups per CU and pick their packs
+                              per thread (see fused_ar_rmsnorm_ex for what that does to `out`) */
 } fused_ar_options;
 
 /*
  * fused_ar_rmsnorm_ex - fused_ar_rmsnorm with `options` (NULL = the defaults, identical to
  * fused_ar_rmsnorm); `path` may also be FUSED_AR_PATH_UNFUSED. Every option combination gives
- * bit-identical residual_out; `out` is bit-identical too unless packs_per_thread changes the
- * order of the row's square-sum (then within the same 1-ulp band). Bad options:
- * FUSED_AR_ERR_INVALID. Otherwise as fused_ar_rmsnorm.
+ * bit-identical residual_out; `out` is bit-identical too unless the row geometry changes - by
+ * packs_per_thread, or by load_policy on calls of more than 1024 rows, whose streaming form takes
+ * its own packs per thread - and with it the order of the row's square-sum (then within the same
+ * 1-ulp band). Bad options: FUSED_AR_ERR_INVALID. Otherwise as fused_ar_rmsnorm.
  */
 int fused_ar_rmsnorm_ex(const fa_bf16 *const *inputs, int n, const fa_bf16 *residual,
                         const fa_bf16 *weight, float eps, int m, int hidden, fa_bf16 *residual_out,
