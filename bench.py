@@ -55,6 +55,9 @@ def parse_args():
                     help="minimum CPU time spent timing the oracle")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only measure path 1 over a grid of row widths and row counts (n = 8): "
+                         "one JSON line per shape")
     ap.add_argument("--all-workloads", action="store_true",
                     help="only measure every workload of the decode/prefill set on each of its "
                          "paths: one JSON line per (workload, m, path)")
@@ -332,6 +335,66 @@ def all_workloads(torch, fa, synth):
             del work
 
 
+class DeviceWorkload(Workload):
+    """A Workload whose buffers are filled on the GPU (seeded normal values), for shapes too large
+    to generate on the host; the timing does not depend on the values."""
+
+    def __init__(self, torch, fa, n, m, hidden, copies, seed=0):
+        self.torch, self.fa, self.lib = torch, fa, fa.library()
+        self.n, self.m, self.hidden, self.eps = n, m, hidden, 1e-6
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(seed)
+        self.weight = (1 + 0.1 * torch.randn(hidden, device="cuda", generator=gen)).to(torch.bfloat16)
+        self.sets = []
+        for c in range(copies):
+            t = [torch.randn(m, hidden, device="cuda", generator=gen).to(torch.bfloat16)
+                 for _ in range(n + 1)]
+            self.sets.append(dict(arr=(ctypes.c_void_p * n)(*[x.data_ptr() for x in t[:-1]]),
+                                  keep=t, res=t[-1].data_ptr(),
+                                  ro_t=torch.empty_like(t[-1]), out_t=torch.empty_like(t[-1])))
+            self.sets[-1]["ro"] = self.sets[-1]["ro_t"].data_ptr()
+            self.sets[-1]["out"] = self.sets[-1]["out_t"].data_ptr()
+        self.ws_bytes = fa.split_workspace_bytes(m, hidden, 0)
+        self.ws = torch.empty(max(self.ws_bytes, 4) // 4, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+
+
+SWEEP_HIDDEN = (2880, 4096, 5120, 7168, 8192, 16384, 32768)
+SWEEP_M = (1, 32, 256, 1024, 4096, 16384)
+
+
+def sweep(torch, fa, n=8):
+    """Path 1 over a grid of row widths and row counts (n = 8): one JSON line per shape. Timing as
+    in all_workloads (warm graphs up to 128 MiB of buffers, HBM-cold rotation above); shapes whose
+    buffers exceed 2 GiB are skipped."""
+    for hidden in SWEEP_HIDDEN:
+        for m in SWEEP_M:
+            footprint = 2 * (n + 3) * m * hidden
+            if footprint > (2 << 30):
+                continue
+            warm = footprint <= (128 << 20)
+            copies = 1 if warm else min(8, max(1, -(-(1 << 30) // footprint)))
+            work = DeviceWorkload(torch, fa, n, m, hidden, copies, seed=hidden + m)
+            bytes_alg = algorithmic_bytes(n, m, hidden)
+            if warm:
+                est_us = 4.0 + bytes_alg / 5e3
+                calls = int(max(50, min(2000, 40e3 / est_us)))
+                us = work.graph_latency_us(1, calls=calls, replays=20)
+                how = f"warm, graph of {calls} calls, min of 20 replays"
+            else:
+                us = work.time_ms(1, 60, 10) * 1e3
+                how = f"60 calls over {copies} buffer sets ({copies * footprint >> 20} MiB)"
+            k = fa.describe_launch(n, m, hidden, 1)["kernels"][0]
+            gbs = bytes_alg / (us * 1e-6) / 1e9
+            print(json.dumps({"n": n, "m": m, "hidden": hidden, "us_per_call": round(us, 3),
+                              "gbs_algorithmic": round(gbs, 1),
+                              "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                              "per_thread": k["per_thread"], "block": k["block"],
+                              "capped": bool(k["lds_bytes"]), "timing": how}), flush=True)
+            del work
+            torch.cuda.empty_cache()
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -358,6 +421,9 @@ def main():
         return
     if args.all_workloads:
         all_workloads(torch, fa, synth)
+        return
+    if args.sweep:
+        sweep(torch, fa)
         return
 
     n, m, hidden, eps, path = args.n, args.m, args.hidden, args.eps, args.path
