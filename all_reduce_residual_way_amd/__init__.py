@@ -204,8 +204,21 @@ def fused_ar_rmsnorm_split_ptrs(input_ptrs, residual, weight, eps, m, hidden, re
                                             int(workspace_bytes), _VP(stream))
 
 
+_torch = None
+
+
+def _torch_module():
+    global _torch
+    if _torch is None:
+        import torch
+        _torch = torch
+    return _torch
+
+
 def _check_tensor(t, name, shape, device):
-    import torch
+    """Raise the error that describes why ``t`` is not a contiguous bf16 tensor of ``shape`` on
+    ``device`` (nothing if it is one)."""
+    torch = _torch_module()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != torch.bfloat16:
@@ -218,31 +231,47 @@ def _check_tensor(t, name, shape, device):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _fits(t, shape, index, torch):
+    """True if ``t`` is a contiguous bf16 CUDA tensor of ``shape`` on device ``index`` (the cheap
+    test made on every call; _check_tensor explains a failure)."""
+    return (isinstance(t, torch.Tensor) and t.dtype is torch.bfloat16 and t.shape == shape
+            and t.get_device() == index and t.is_contiguous())
+
+
 def _stream_handle(stream, device):
-    import torch
-    if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return stream.cuda_stream
+    torch = _torch_module()
+    if stream is not None:
+        return stream.cuda_stream
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)  # no Stream object per call
+    if raw is not None:
+        return raw(device.index)
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _prepare(inputs, residual, weight, residual_out, out):
-    import torch
+    torch = _torch_module()
     if not isinstance(inputs, (list, tuple)) or not inputs:
         raise ValueError("inputs must be a non-empty list of tensors")
     if not isinstance(residual, torch.Tensor) or residual.dim() != 2:
         raise ValueError("residual must be a 2-D tensor (m, hidden)")
-    m, hidden = residual.shape
+    shape = residual.shape
+    m, hidden = shape
     device = residual.device
-    for i, x in enumerate(inputs):
-        _check_tensor(x, f"inputs[{i}]", (m, hidden), device)
-    _check_tensor(residual, "residual", (m, hidden), device)
-    _check_tensor(weight, "weight", (hidden,), device)
+    index = device.index if device.type == "cuda" else -2  # get_device() is -1 on the CPU
+    if not (all(_fits(x, shape, index, torch) for x in inputs)
+            and _fits(residual, shape, index, torch) and _fits(weight, (hidden,), index, torch)):
+        for i, x in enumerate(inputs):
+            _check_tensor(x, f"inputs[{i}]", (m, hidden), device)
+        _check_tensor(residual, "residual", (m, hidden), device)
+        _check_tensor(weight, "weight", (hidden,), device)
     if residual_out is None:
         residual_out = torch.empty_like(residual)
+    elif not _fits(residual_out, shape, index, torch):
+        _check_tensor(residual_out, "residual_out", (m, hidden), device)
     if out is None:
         out = torch.empty_like(residual)
-    _check_tensor(residual_out, "residual_out", (m, hidden), device)
-    _check_tensor(out, "out", (m, hidden), device)
+    elif not _fits(out, shape, index, torch):
+        _check_tensor(out, "out", (m, hidden), device)
     return m, hidden, device, residual_out, out
 
 
@@ -268,9 +297,12 @@ def fused_ar_rmsnorm(inputs, residual, weight, eps=1e-6, *, residual_out=None, o
         FusedArError for a non-zero library status.
     """
     m, hidden, device, residual_out, out = _prepare(inputs, residual, weight, residual_out, out)
-    rc = fused_ar_rmsnorm_ex_ptrs([x.data_ptr() for x in inputs], residual.data_ptr(),
-                                  weight.data_ptr(), eps, m, hidden, residual_out.data_ptr(),
-                                  out.data_ptr(), path, options, _stream_handle(stream, device))
+    n = len(inputs)
+    arr = (_VP * n)(*[x.data_ptr() for x in inputs])
+    rc = library().fused_ar_rmsnorm_ex(arr, n, residual.data_ptr(), weight.data_ptr(), eps, m,
+                                       hidden, residual_out.data_ptr(), out.data_ptr(), path,
+                                       None if options is None else ctypes.byref(options),
+                                       _stream_handle(stream, device))
     if rc != OK:
         raise FusedArError(rc, "fused_ar_rmsnorm")
     return residual_out, out
