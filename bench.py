@@ -223,6 +223,18 @@ def host_threads():
     return max(1, min(16, have))
 
 
+def host_cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None where there is no such file)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def oracle_all_cores(oracle, prob, eps, bytes_alg, seconds):
     """The unchanged oracle on row slices, one slice per host thread (ctypes drops the GIL).
 
@@ -543,7 +555,7 @@ def main():
             if elapsed >= args.cpu_seconds:
                 break
         cpu = {"value": round(passes * bytes_alg / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1,
-               "kind": "oracle",
+               "kind": "oracle", "cpu": host_cpu_model(),
                "sample": f"the whole timed workload (n={n}, m={m}, hidden={hidden}), {passes} "
                          f"pass(es) in {elapsed:.1f} s, single-threaded C oracle"}
         if not args.no_extra:
