@@ -368,3 +368,17 @@ def test_row_workgroups_capped_on_long_streaming_calls():
     assert lds(8, 1025, 8192) == [64 * 1024]
     assert lds(8, 32, 7168) == [0]
     assert lds(8, 4096, 7168, 1, fa.Options(0, 0, 0, 0, fa.LOAD_CACHED)) == [0]
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built library every entry point raises; nothing falls back to other code."""
+    import torch
+    monkeypatch.setattr(fa, "_lib", None)
+    monkeypatch.setattr(fa, "LIBRARY_PATH", str(tmp_path / "libfused_ar.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        fa.library()
+    with pytest.raises(RuntimeError, match="not built"):
+        fa.auto_path(8, 1, 7168)
+    x = torch.zeros(4, 16, dtype=torch.bfloat16)
+    with pytest.raises((RuntimeError, ValueError)):  # CPU tensors: rejected, never computed
+        fa.fused_ar_rmsnorm([x], x, torch.zeros(16, dtype=torch.bfloat16))
