@@ -354,6 +354,10 @@ def fused_ar_rmsnorm_split(inputs, residual, weight, eps=1e-6, *, splits=0, work
     need = split_workspace_bytes(m, hidden, splits)
     if workspace is None:
         workspace = torch.empty(max(need, 4) // 4, dtype=torch.float32, device=device)
+        if stream is not None:
+            # allocated for the current stream but used on `stream`: keep the caching allocator
+            # from handing it out again before the work on `stream` is done
+            workspace.record_stream(stream)
     if not isinstance(workspace, torch.Tensor) or workspace.device != device:
         raise ValueError(f"workspace must be a tensor on {device}")
     if not workspace.is_contiguous():

@@ -363,6 +363,39 @@ def test_graph_replay_matches_eager():
     assert_parity("graph", host(ro), host(out), want_ro, want_out)
 
 
+def test_concurrent_calls_on_two_streams():
+    """The library keeps no state, so calls enqueued on two streams at once, on separate buffers
+    and on every path, each give the oracle's result."""
+    probs = [synth.make_problem(8, 300, 7168, seed=16), synth.make_problem(4, 17, 2880, seed=17)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    bufs = []
+    for p in probs:
+        ins = [dev(x) for x in p.inputs]
+        res, w = dev(p.residual), dev(p.weight)
+        outs = {path: (torch.empty_like(res), torch.empty_like(res)) for path in (1, 2, "split")}
+        bufs.append((ins, res, w, outs))
+    torch.cuda.synchronize()
+    announce("two streams, 10 rounds of every path")
+    def enqueue(ins, res, w, outs, p, stream):
+        for path, (ro, out) in outs.items():
+            if path == "split":  # the workspace is allocated by the binding
+                fa.fused_ar_rmsnorm_split(ins, res, w, p.eps, residual_out=ro, out=out,
+                                          stream=stream)
+            else:
+                fa.fused_ar_rmsnorm(ins, res, w, p.eps, residual_out=ro, out=out, path=path,
+                                    stream=stream)
+
+    for _ in range(10):
+        with torch.cuda.stream(streams[0]):  # the first problem: the current stream
+            enqueue(*bufs[0], probs[0], None)
+        enqueue(*bufs[1], probs[1], streams[1])  # the second: an explicit stream argument
+    torch.cuda.synchronize()
+    for (ins, res, w, outs), p in zip(bufs, probs):
+        want_ro, want_out = oracle_rows(p)
+        for path, (ro, out) in outs.items():
+            assert_parity(f"stream n={p.n} path={path}", host(ro), host(out), want_ro, want_out)
+
+
 # ------------------------------------------------------------------------- unfused baseline
 
 @pytest.mark.parametrize("n,m,hidden", [(8, 16, 7168), (4, 300, 7168), (8, 33, 2880), (3, 5, 520),
