@@ -8,6 +8,7 @@ streams. If the library is not built, every call raises; there is no fallback.
     from all_reduce_residual_way_amd import fused_ar_rmsnorm
     residual_out, out = fused_ar_rmsnorm(inputs, residual, weight, eps=1e-6)
 """
+import contextlib
 import ctypes
 import os
 
@@ -238,6 +239,18 @@ def _fits(t, shape, index, torch):
             and t.get_device() == index and t.is_contiguous())
 
 
+_NO_GUARD = contextlib.nullcontext()
+
+
+def _device_guard(device):
+    """Makes ``device`` the current device for the call (the library launches on the current
+    device, and the default stream handle 0 means that device's null stream); no-op if it is."""
+    torch = _torch_module()
+    if device.index == torch.cuda.current_device():
+        return _NO_GUARD
+    return torch.cuda.device(device.index)
+
+
 def _stream_handle(stream, device):
     torch = _torch_module()
     if stream is not None:
@@ -299,10 +312,11 @@ def fused_ar_rmsnorm(inputs, residual, weight, eps=1e-6, *, residual_out=None, o
     m, hidden, device, residual_out, out = _prepare(inputs, residual, weight, residual_out, out)
     n = len(inputs)
     arr = (_VP * n)(*[x.data_ptr() for x in inputs])
-    rc = library().fused_ar_rmsnorm_ex(arr, n, residual.data_ptr(), weight.data_ptr(), eps, m,
-                                       hidden, residual_out.data_ptr(), out.data_ptr(), path,
-                                       None if options is None else ctypes.byref(options),
-                                       _stream_handle(stream, device))
+    with _device_guard(device):
+        rc = library().fused_ar_rmsnorm_ex(arr, n, residual.data_ptr(), weight.data_ptr(), eps, m,
+                                           hidden, residual_out.data_ptr(), out.data_ptr(), path,
+                                           None if options is None else ctypes.byref(options),
+                                           _stream_handle(stream, device))
     if rc != OK:
         raise FusedArError(rc, "fused_ar_rmsnorm")
     return residual_out, out
@@ -313,9 +327,11 @@ def fused_ar_unfused_rmsnorm(inputs, residual, weight, eps=1e-6, *, residual_out
     """The same result as fused_ar_rmsnorm, computed as three kernels (reduce, residual add,
     RMSNorm): the unfused baseline. Arguments and returns as fused_ar_rmsnorm (no path)."""
     m, hidden, device, residual_out, out = _prepare(inputs, residual, weight, residual_out, out)
-    rc = fused_ar_unfused_rmsnorm_ptrs([x.data_ptr() for x in inputs], residual.data_ptr(),
-                                       weight.data_ptr(), eps, m, hidden, residual_out.data_ptr(),
-                                       out.data_ptr(), _stream_handle(stream, device))
+    with _device_guard(device):
+        rc = fused_ar_unfused_rmsnorm_ptrs([x.data_ptr() for x in inputs], residual.data_ptr(),
+                                           weight.data_ptr(), eps, m, hidden,
+                                           residual_out.data_ptr(), out.data_ptr(),
+                                           _stream_handle(stream, device))
     if rc != OK:
         raise FusedArError(rc, "fused_ar_unfused_rmsnorm")
     return residual_out, out
@@ -336,8 +352,9 @@ def fused_ar_reduce(inputs, *, reduced=None, stream=None):
     if reduced is None:
         reduced = torch.empty_like(x0)
     _check_tensor(reduced, "reduced", (m, hidden), x0.device)
-    rc = fused_ar_reduce_ptrs([x.data_ptr() for x in inputs], m, hidden, reduced.data_ptr(),
-                              _stream_handle(stream, x0.device))
+    with _device_guard(x0.device):
+        rc = fused_ar_reduce_ptrs([x.data_ptr() for x in inputs], m, hidden, reduced.data_ptr(),
+                                  _stream_handle(stream, x0.device))
     if rc != OK:
         raise FusedArError(rc, "fused_ar_reduce")
     return reduced
@@ -363,10 +380,12 @@ def fused_ar_rmsnorm_split(inputs, residual, weight, eps=1e-6, *, splits=0, work
     if not workspace.is_contiguous():
         raise ValueError("workspace must be contiguous")
     nbytes = workspace.numel() * workspace.element_size()
-    rc = fused_ar_rmsnorm_split_ptrs([x.data_ptr() for x in inputs], residual.data_ptr(),
-                                     weight.data_ptr(), eps, m, hidden, residual_out.data_ptr(),
-                                     out.data_ptr(), splits, workspace.data_ptr(), nbytes,
-                                     _stream_handle(stream, device))
+    with _device_guard(device):
+        rc = fused_ar_rmsnorm_split_ptrs([x.data_ptr() for x in inputs], residual.data_ptr(),
+                                         weight.data_ptr(), eps, m, hidden,
+                                         residual_out.data_ptr(), out.data_ptr(), splits,
+                                         workspace.data_ptr(), nbytes,
+                                         _stream_handle(stream, device))
     if rc != OK:
         raise FusedArError(rc, "fused_ar_rmsnorm_split")
     return residual_out, out
