@@ -449,8 +449,7 @@ def main():
     ms = work.time_ms(path, args.steps, args.warmup)
     gbs = bytes_alg / (ms * 1e-3) / 1e9
 
-    # sampled parity of the timed configuration against the oracle (rows are independent)
-    import oracle
+    # the timed configuration's output rows, checked against the oracle in the CPU leg below
     rows = parity_rows(m)
 
     def host_rows(t):  # row slices are bounds-checked on the host; no device-side gather
@@ -459,11 +458,6 @@ def main():
 
     got_ro = host_rows(work.sets[0]["ro_t"])
     got_out = host_rows(work.sets[0]["out_t"])
-    want_ro, want_out = oracle.fused([x[rows] for x in prob.inputs], prob.residual[rows],
-                                     prob.weight, eps)
-    ords = [np.where(b & 0x8000, -(b & 0x7FFF).astype(np.int32), b.astype(np.int32))
-            for b in (got_out, want_out)]
-    parity_ok = bool(np.array_equal(got_ro, want_ro) and np.abs(ords[0] - ords[1]).max() <= 1)
 
     def entry(p, pms):
         return {"us_per_call": round(pms * 1e3, 3),
@@ -545,7 +539,16 @@ def main():
                     del dw
 
     cpu = None
+    parity_ok = None
     if not args.no_cpu:
+        # The CPU leg: the oracle (test infrastructure, used nowhere else here) checks the sampled
+        # rows of the timed configuration (rows are independent), then is timed on the host.
+        import oracle
+        want_ro, want_out = oracle.fused([x[rows] for x in prob.inputs], prob.residual[rows],
+                                         prob.weight, eps)
+        ords = [np.where(b & 0x8000, -(b & 0x7FFF).astype(np.int32), b.astype(np.int32))
+                for b in (got_out, want_out)]
+        parity_ok = bool(np.array_equal(got_ro, want_ro) and np.abs(ords[0] - ords[1]).max() <= 1)
         log(f"timing the CPU oracle for at least {args.cpu_seconds:.0f} s")
         passes, t0 = 0, time.perf_counter()
         while True:
