@@ -727,7 +727,10 @@ extern "C" const char *fused_ar_strerror(int status)
     switch (status) {
     case FUSED_AR_OK: return "success";
     case FUSED_AR_ERR_INVALID: return "invalid argument (null pointer, n, m, hidden, eps, path or option out of range)";
-    case FUSED_AR_ERR_SHAPE: return "unsupported shape (hidden must be a multiple of 8 and at most 32768)";
+    case FUSED_AR_ERR_SHAPE:
+        return "unsupported shape (hidden must be a multiple of 8 and at most 32768, and a row, or a "
+               "slice of a split row, must fit one 1024-thread workgroup at the packs per thread or "
+               "slice count asked for)";
     case FUSED_AR_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
     case FUSED_AR_ERR_ALIAS: return "forbidden overlap between output and other buffers";
     default: break;

@@ -47,7 +47,9 @@ enum {
     FUSED_AR_OK = 0,
     FUSED_AR_ERR_INVALID = -1, /* null pointer, n outside [1, 8], m < 0, hidden <= 0, eps < 0 or
                                   not finite, path outside {0, 1, 2}, pointer range wraps */
-    FUSED_AR_ERR_SHAPE = -2,   /* hidden not a multiple of 8, or above FUSED_AR_MAX_HIDDEN */
+    FUSED_AR_ERR_SHAPE = -2,   /* hidden not a multiple of 8, or above FUSED_AR_MAX_HIDDEN; or a
+                                  row (slice) that does not fit 1024 threads at the packs per
+                                  thread (slices) a caller forced */
     FUSED_AR_ERR_ALIGN = -3,   /* a device pointer not 16-byte aligned */
     FUSED_AR_ERR_ALIAS = -4    /* a forbidden overlap of buffers (see fused_ar_rmsnorm) */
 };
