@@ -68,3 +68,106 @@ def test_checks_follow_the_documented_rules(n, m, hidden, eps, path, ins, res, w
     got = fa.fused_ar_rmsnorm_check_ptrs(ins, res, w, eps, m, hidden, ro, out, path)
     assert got == want, (n, m, hidden, eps, path, [hex(p) for p in ins], hex(res), hex(w),
                          hex(ro), hex(out))
+
+
+# ------------------------------------------------------------------------- launch plans
+
+ROWS_PER_LAUNCH = 1 << 20
+FLAT_PACKS_PER_LAUNCH = 1 << 30
+
+
+def expected_streaming(n, m, hidden, policy):
+    """Load policy: forced, or streaming when a call reads more than 128 MiB (inputs + residual)."""
+    if policy != fa.LOAD_AUTO:
+        return policy == fa.LOAD_STREAM
+    return 2 * (n + 1) * m * hidden > (128 << 20)
+
+
+def expected_rows(packs, m, forced, capped):
+    """Packs per thread and threads of the row kernel, or None where a forced value does not fit."""
+    if forced:
+        k = forced
+        if (packs + k - 1) // k > 1024:
+            return None
+    else:
+        if capped:
+            k = 4 if packs > 1024 else (2 if packs >= 512 else 1)
+        else:
+            k = 2 if (257 <= m <= 1024 and packs > 512) else 1
+        while k < 4 and (packs + k - 1) // k > 1024:
+            k *= 2
+    t = (packs + k - 1) // k
+    return k, (t + 63) // 64 * 64
+
+
+@settings(max_examples=3000, deadline=None)
+@given(n=st.integers(min_value=1, max_value=8),
+       m=st.one_of(st.sampled_from([0, 1, 16, 17, 32, 33, 256, 257, 1024, 1025, 4096]),
+                   st.integers(min_value=0, max_value=40), st.integers(min_value=0, max_value=5000),
+                   st.integers(min_value=(1 << 20) - 2, max_value=(1 << 20) + 2),
+                   st.integers(min_value=0, max_value=1 << 22)),
+       packs=st.one_of(st.integers(min_value=1, max_value=4096),
+                       st.sampled_from([360, 511, 512, 896, 1024, 1025, 2048, 4096])),
+       path=st.integers(min_value=0, max_value=3),
+       wave=st.integers(min_value=0, max_value=1), stage1=st.integers(min_value=0, max_value=1),
+       block=st.sampled_from([0, 64, 256, 512, 1024]), ppt=st.sampled_from([0, 1, 2, 4]),
+       policy=st.integers(min_value=0, max_value=2))
+def test_launch_plans_follow_the_geometry_rules(n, m, packs, path, wave, stage1, block, ppt,
+                                                policy):
+    check_plan(n, m, packs, path, wave, stage1, block, ppt, policy)
+
+
+def test_launch_plans_on_the_rule_boundaries():
+    """Every combination of the values where a rule changes, so that each boundary is checked
+    whatever the random examples above happen to draw."""
+    import itertools
+    for n, m, packs, path, stage1, block, ppt, policy in itertools.product(
+            (1, 4, 5, 8), (0, 1, 16, 17, 32, 33, 256, 257, 1024, 1025, 2048, 4096, 9000),
+            (1, 360, 511, 512, 513, 896, 1024, 1025, 2048, 4096), (0, 1, 2, 3), (0, 1),
+            (0, 256), (0, 1, 2, 4), (0, 1, 2)):
+        check_plan(n, m, packs, path, 0, stage1, block, ppt, policy)
+
+
+def check_plan(n, m, packs, path, wave, stage1, block, ppt, policy):
+    hidden = 8 * packs
+    opt = fa.Options(wave, stage1, block, ppt, policy)
+    stream = expected_streaming(n, m, hidden, policy)
+    capped = stream and m > 1024
+    rows = expected_rows(packs, m, ppt, capped)
+    if m > 0 and rows is None:
+        with pytest.raises(fa.FusedArError) as e:
+            fa.describe_launch(n, m, hidden, path, opt)
+        assert e.value.status == fa.ERR_SHAPE
+        return
+    plan = fa.describe_launch(n, m, hidden, path, opt)
+    want_path = path if path else (1 if m <= (32 if n <= 4 else 16) else 2)
+    assert plan["path"] == want_path
+    if m == 0:
+        assert plan["kernels"] == []
+        return
+    ks = plan["kernels"]
+    assert [k["name"] for k in ks] == {
+        1: ["onestage"],
+        2: ["stage1_reduce_lds" if stage1 else "stage1_reduce", "stage2_norm"],
+        3: ["stage1_reduce_lds" if stage1 else "stage1_reduce", "residual_add", "rmsnorm"]}[want_path]
+    # the row kernel: one workgroup per row, whole waves, every pack of a row covered once
+    k_rows = ks[-1]
+    assert (k_rows["per_thread"], k_rows["block"]) == rows
+    assert k_rows["grid"] == min(m, ROWS_PER_LAUNCH)
+    assert k_rows["launches"] == -(-m // ROWS_PER_LAUNCH)
+    assert k_rows["lds_bytes"] == (64 * 1024 if capped else 0)
+    assert k_rows["streaming"] == int(stream)
+    # the flat kernels: one pack per thread over all m * packs packs
+    total = m * packs
+    for k in ks[:-1]:
+        if k["name"] == "stage1_reduce_lds":
+            want_block = 64 * n
+        elif block:
+            want_block = block
+        else:
+            want_block = 512 if total >= (1 << 20) else 256
+        assert k["block"] == want_block and k["per_thread"] == 1
+        first = min(total, FLAT_PACKS_PER_LAUNCH)
+        assert k["grid"] == -(-first // want_block)
+        assert k["launches"] == -(-total // FLAT_PACKS_PER_LAUNCH)
+        assert k["lds_bytes"] == 0 and k["streaming"] == int(stream)
