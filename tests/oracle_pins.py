@@ -11,7 +11,6 @@ test_oracle_pins.py runs them on the oracle; test_oracle_mutants.py runs them on
 oracle with planted mistakes and requires each mistake to fail at least one of them.
 """
 import itertools
-import struct
 from fractions import Fraction
 
 import numpy as np
