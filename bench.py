@@ -56,8 +56,8 @@ def parse_args():
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     ap.add_argument("--sweep", action="store_true",
-                    help="only measure path 1 over a grid of row widths and row counts (n = 8): "
-                         "one JSON line per shape")
+                    help="only measure path 1 over a grid of row widths and row counts (--n "
+                         "inputs, default 8): one JSON line per shape")
     ap.add_argument("--all-workloads", action="store_true",
                     help="only measure every workload of the decode/prefill set on each of its "
                          "paths: one JSON line per (workload, m, path)")
@@ -376,9 +376,9 @@ SWEEP_M = (1, 32, 256, 1024, 4096, 16384)
 
 
 def sweep(torch, fa, n=8):
-    """Path 1 over a grid of row widths and row counts (n = 8): one JSON line per shape. Timing as
-    in all_workloads (warm graphs up to 128 MiB of buffers, HBM-cold rotation above); shapes whose
-    buffers exceed 2 GiB are skipped."""
+    """Path 1 over a grid of row widths and row counts (n inputs, from --n): one JSON line per
+    shape. Timing as in all_workloads (warm graphs up to 128 MiB of buffers, HBM-cold rotation
+    above); shapes whose buffers exceed 2 GiB are skipped."""
     for hidden in SWEEP_HIDDEN:
         for m in SWEEP_M:
             footprint = 2 * (n + 3) * m * hidden
@@ -435,7 +435,7 @@ def main():
         all_workloads(torch, fa, synth)
         return
     if args.sweep:
-        sweep(torch, fa)
+        sweep(torch, fa, n=args.n)
         return
 
     n, m, hidden, eps, path = args.n, args.m, args.hidden, args.eps, args.path
