@@ -73,6 +73,13 @@ def library():
             raise RuntimeError(
                 f"{LIBRARY_PATH} is not built; build it with "
                 "`python all_reduce_residual_way_amd/build.py`")
+        # torch ships its own HIP runtime (same soname as ROCm's). Loading it first makes this
+        # library bind to it; loaded the other way round, the process would hold two HIP and two
+        # HSA runtimes, and the second to open the GPU finds no device.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         lib = ctypes.CDLL(LIBRARY_PATH)
         lib.fused_ar_rmsnorm.argtypes = [ctypes.POINTER(_VP), ctypes.c_int, _VP, _VP, ctypes.c_float,
                                          ctypes.c_int, ctypes.c_int, _VP, _VP, ctypes.c_int, _VP]

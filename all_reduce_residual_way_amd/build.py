@@ -9,6 +9,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 SOURCES = [os.path.join(CSRC, "fused_ar.hip")]
 LIBRARY = os.path.join(PKG, "libfused_ar.so")
+# HBM ceiling probes for the benchmark (not part of the fused path)
+PROBE_SOURCES = [os.path.join(CSRC, "hbm_probe.hip")]
+PROBE_LIBRARY = os.path.join(PKG, "libhbm_probe.so")
 ARCH = "gfx950"
 
 FLAGS = [
@@ -28,10 +31,10 @@ def hipcc():
     return path
 
 
-def build(output=LIBRARY, extra_flags=(), verbose=False):
-    """Compile every HIP source into ``output``; returns its path. Always recompiles."""
+def build(output=LIBRARY, extra_flags=(), verbose=False, sources=SOURCES):
+    """Compile the HIP ``sources`` into ``output``; returns its path. Always recompiles."""
     tmp = output + ".tmp"
-    cmd = [hipcc(), *FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *SOURCES]
+    cmd = [hipcc(), *FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
@@ -39,5 +42,11 @@ def build(output=LIBRARY, extra_flags=(), verbose=False):
     return output
 
 
+def build_probe(verbose=False):
+    """Compile the HBM ceiling probes into libhbm_probe.so; returns its path."""
+    return build(PROBE_LIBRARY, verbose=verbose, sources=PROBE_SOURCES)
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_probe(verbose=True))

@@ -55,6 +55,9 @@ def parse_args():
                     help="minimum CPU time spent timing the oracle")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure plain read, copy and 9-read/2-write streaming kernels "
+                         "(practical HBM ceilings): one JSON line per measurement")
     ap.add_argument("--sweep", action="store_true",
                     help="only measure path 1 over a grid of row widths and row counts (--n "
                          "inputs, default 8): one JSON line per shape")
@@ -119,6 +122,95 @@ def copy_calibration(torch):
     print(json.dumps({"copy_calibration": {"bytes_read": nbytes, "bytes_written": nbytes,
                                            "launches": 5, "ms_per_copy": ms,
                                            "gbs": 2 * nbytes / ms / 1e9 * 1e3}}), flush=True)
+
+
+def hbm_ceilings(torch):
+    """Practical HBM ceilings on this GPU from the plain streaming kernels of libhbm_probe.so: one
+    read stream, a copy, and the one-stage kernel's mix of nine read and two write streams at its
+    bench shape (N=8, m=4096, hidden=7168), each over a few launch shapes and cache policies,
+    HBM-cold (4 GiB read buffer; 2 GiB copies; two alternating mix sets of 646 MB); then the
+    one-stage kernel itself on that shape in the same process. One JSON line per measurement, then
+    a summary line with the best of each and the kernel's rate over the best mix."""
+    import ctypes
+    from all_reduce_residual_way_amd import build as hip_build
+    if not os.path.exists(hip_build.PROBE_LIBRARY):
+        raise RuntimeError(f"{hip_build.PROBE_LIBRARY} is not built")
+    lib = ctypes.CDLL(hip_build.PROBE_LIBRARY)
+    vp, sz, ci = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.hbm_probe_read.argtypes = [vp, sz, vp, ci, ci, ci, vp]
+    lib.hbm_probe_copy.argtypes = [vp, vp, sz, ci, ci, vp]
+    lib.hbm_probe_mix.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), sz, ci, ci, vp]
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def timed_ms(fn, reps):
+        for _ in range(3):
+            fn(0)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(reps):
+            fn(i)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / reps
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(f"HBM probe failed with status {rc}")
+
+    best = {}
+
+    def report(kind, nbytes, ms, **shape):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        best[kind] = max(best.get(kind, 0.0), gbs)
+        print(json.dumps({"probe": kind, **shape, "bytes": nbytes, "us": round(ms * 1e3, 2),
+                          "gbs": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1)}),
+              flush=True)
+
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(3)
+    sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    for nt in (1, 0):
+        for unroll, grid in ((1, 2048), (8, 8192), (8, 32768)):
+            ms = timed_ms(lambda i: check(lib.hbm_probe_read(buf.data_ptr(), nbytes // 16,
+                                                             sink.data_ptr(), nt, unroll, grid,
+                                                             stream)), 20)
+            report("read", nbytes, ms, nt=nt, unroll=unroll, grid=grid)
+    half = nbytes // 2
+    for nt in (3, 1):  # non-temporal loads, with non-temporal or ordinary stores
+        for grid in (8192, 65536):
+            ms = timed_ms(lambda i: check(lib.hbm_probe_copy(buf.data_ptr(), buf.data_ptr() + half,
+                                                             half // 16, nt, grid, stream)), 20)
+            report("copy", 2 * half, ms, nt=nt, grid=grid)
+    del buf
+    torch.cuda.empty_cache()
+    n, m, hidden = 8, 4096, 7168
+    plane = m * hidden * 2
+    sets = []
+    for _ in range(2):
+        t = torch.empty(11 * plane, dtype=torch.uint8, device="cuda")
+        t.fill_(1)
+        ins = (vp * 9)(*[t.data_ptr() + k * plane for k in range(9)])
+        outs = (vp * 2)(*[t.data_ptr() + (9 + k) * plane for k in range(2)])
+        sets.append((t, ins, outs))
+    for nt in (3, 1):
+        for grid in (8192, 14336):
+            ms = timed_ms(lambda i: check(lib.hbm_probe_mix(sets[i % 2][1], sets[i % 2][2],
+                                                            plane // 16, nt, grid, stream)), 40)
+            report("mix9r2w", 11 * plane, ms, nt=nt, grid=grid)
+    del sets
+    torch.cuda.empty_cache()
+    # the one-stage kernel on the same traffic, in the same process, for a side-by-side ratio
+    import all_reduce_residual_way_amd as fa
+    work = DeviceWorkload(torch, fa, n, m, hidden, 2, seed=1)
+    ms = work.time_ms(1, 200, 20)
+    report("onestage", algorithmic_bytes(n, m, hidden), ms, n=n, m=m, hidden=hidden)
+    print(json.dumps({"hbm_ceilings_gbs": {k: round(v, 1) for k, v in best.items()},
+                      "pct_of_hbm_peak": {k: round(100 * v / HBM_PEAK_GBS, 1)
+                                          for k, v in best.items()},
+                      "onestage_over_mix9r2w": round(best["onestage"] / best["mix9r2w"], 3)}),
+          flush=True)
 
 
 class Workload:
@@ -433,6 +525,9 @@ def main():
         return
     if args.all_workloads:
         all_workloads(torch, fa, synth)
+        return
+    if args.ceilings:
+        hbm_ceilings(torch)
         return
     if args.sweep:
         sweep(torch, fa, n=args.n)

@@ -382,3 +382,19 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     x = torch.zeros(4, 16, dtype=torch.bfloat16)
     with pytest.raises((RuntimeError, ValueError)):  # CPU tensors: rejected, never computed
         fa.fused_ar_rmsnorm([x], x, torch.zeros(16, dtype=torch.bfloat16))
+
+
+def test_one_hip_runtime_per_process():
+    """Loading the library in a fresh process that has not imported torch, then using torch, leaves
+    a single HIP runtime mapped (torch's): two runtimes in one process cannot both open the GPU."""
+    import ast
+    import subprocess
+    import sys
+    code = ("import all_reduce_residual_way_amd as fa; fa.library(); import torch; "
+            "maps = open('/proc/self/maps').read(); "
+            "print(sorted({l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l}))")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                       cwd=ROOT)
+    assert r.returncode == 0, r.stderr
+    runtimes = ast.literal_eval(r.stdout.strip().splitlines()[-1])
+    assert len(runtimes) == 1, runtimes

@@ -1,0 +1,85 @@
+"""The HBM ceiling probes of the benchmark (libhbm_probe.so): argument checks on the CPU (no kernel is
+launched), and on the GPU that each probe moves exactly the bytes it claims to (copy, XOR/add mix),
+so the ceilings the benchmark reports are measured on correct streaming kernels."""
+import ctypes
+import os
+
+import pytest
+import torch  # before the probe library, so that it binds to torch's HIP runtime
+
+from all_reduce_residual_way_amd import build as hip_build
+
+VP, SZ, CI = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+FAKE = 0x7F0000000000  # aligned, never dereferenced: every call below is rejected before a launch
+
+
+@pytest.fixture(scope="module")
+def probe():
+    if not os.path.exists(hip_build.PROBE_LIBRARY):
+        pytest.fail(f"{hip_build.PROBE_LIBRARY} is not built")
+    lib = ctypes.CDLL(hip_build.PROBE_LIBRARY)
+    lib.hbm_probe_read.argtypes = [VP, SZ, VP, CI, CI, CI, VP]
+    lib.hbm_probe_copy.argtypes = [VP, VP, SZ, CI, CI, VP]
+    lib.hbm_probe_mix.argtypes = [ctypes.POINTER(VP), ctypes.POINTER(VP), SZ, CI, CI, VP]
+    return lib
+
+
+def test_probe_arguments_rejected_before_launch(probe):
+    assert probe.hbm_probe_read(None, 16, FAKE, 1, 8, 64, None) == -1
+    assert probe.hbm_probe_read(FAKE, 0, FAKE, 1, 8, 64, None) == -1
+    assert probe.hbm_probe_read(FAKE + 8, 16, FAKE, 1, 8, 64, None) == -1
+    assert probe.hbm_probe_read(FAKE, 16, FAKE, 1, 3, 64, None) == -1   # unroll not 1, 4 or 8
+    assert probe.hbm_probe_read(FAKE, 16, FAKE, 0, 8, 0, None) == -1    # empty grid
+    assert probe.hbm_probe_read(FAKE, 16, FAKE, 4, 8, 64, None) == -1   # cache policy 0..3
+    assert probe.hbm_probe_copy(FAKE, FAKE, 16, -1, 64, None) == -1
+    assert probe.hbm_probe_copy(FAKE, None, 16, 1, 64, None) == -1
+    assert probe.hbm_probe_copy(FAKE, FAKE, 16, 1, (1 << 20) + 1, None) == -1
+    ins = (VP * 9)(*([FAKE] * 8 + [None]))
+    outs = (VP * 2)(FAKE, FAKE)
+    assert probe.hbm_probe_mix(ins, outs, 16, 1, 64, None) == -1
+    ins = (VP * 9)(*([FAKE] * 9))
+    outs = (VP * 2)(FAKE, FAKE + 4)
+    assert probe.hbm_probe_mix(ins, outs, 16, 1, 64, None) == -1
+
+
+@pytest.mark.gpu
+def test_probes_move_the_bytes_they_claim(probe):
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    print("[gpu case] HBM probes: read, copy, mix on 1 MiB streams", flush=True)
+    stream = torch.cuda.current_stream().cuda_stream
+    g = torch.Generator(device="cpu").manual_seed(11)
+    packs = (1 << 20) // 16 + 3  # a ragged tail for the grid-stride loops
+    words = packs * 4
+
+    def rand_words():
+        return torch.randint(-2**31, 2**31, (words,), generator=g, dtype=torch.int64) \
+            .to(torch.int32).cuda()
+
+    src = rand_words()
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for nt in (0, 1):
+        for unroll in (1, 4, 8):
+            assert probe.hbm_probe_read(src.data_ptr(), packs, sink.data_ptr(), nt, unroll, 37,
+                                        stream) == 0
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum()) == 0  # random data never hits the fold's fixed pattern
+
+    for nt in range(4):
+        dst = torch.zeros_like(src)
+        assert probe.hbm_probe_copy(src.data_ptr(), dst.data_ptr(), packs, nt, 37, stream) == 0
+        torch.cuda.synchronize()
+        assert torch.equal(dst, src)
+
+    ins_t = [rand_words() for _ in range(9)]
+    x = ins_t[0].clone()
+    for t in ins_t[1:]:
+        x = torch.bitwise_xor(x, t)
+    want1 = (x.to(torch.int64) + ins_t[0].to(torch.int64)).remainder(2**32)
+    for nt in range(4):
+        outs_t = [torch.zeros_like(src) for _ in range(2)]
+        ins = (VP * 9)(*[t.data_ptr() for t in ins_t])
+        outs = (VP * 2)(*[t.data_ptr() for t in outs_t])
+        assert probe.hbm_probe_mix(ins, outs, packs, nt, 37, stream) == 0
+        torch.cuda.synchronize()
+        assert torch.equal(outs_t[0], x)
+        assert torch.equal(outs_t[1].to(torch.int64).remainder(2**32), want1)
