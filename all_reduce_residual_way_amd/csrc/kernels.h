@@ -94,9 +94,9 @@ __device__ __forceinline__ u32x4 normalise(const F8 &y, const F8 &g, float rstd)
 // arguments, possible only with eps = 0 or eps subnormal, keep the same accuracy; 0 gives +inf.
 __device__ __forceinline__ float rsqrt_f32(float v)
 {
-    if (v >= 0x1p-126f)
-        return __builtin_amdgcn_rsqf(v);
-    return 0x1p12f * __builtin_amdgcn_rsqf(v * 0x1p24f);
+    const bool tiny = v < 0x1p-126f;
+    const float r = __builtin_amdgcn_rsqf(tiny ? v * 0x1p24f : v);
+    return tiny ? 0x1p12f * r : r;
 }
 
 // A pack at a byte offset from a wave-uniform base (the base stays in scalar registers, the
