@@ -1,5 +1,5 @@
 // hbm_probe.hip - libhbm_probe.so: plain streaming kernels that measure what HBM delivers on this
-// GPU for three traffic mixes, as the practical ceilings the fused kernel is judged against:
+// GPU for three traffic mixes, as the practical ceilings the fused kernel is compared with:
 //   read  - one read stream (every 16-byte pack XOR-folded into a register; nothing is written
 //           unless the fold hits a fixed 128-bit pattern, so the loads cannot be removed)
 //   copy  - one read and one write stream
