@@ -99,6 +99,21 @@ __device__ __forceinline__ float rsqrt_f32(float v)
     return tiny ? 0x1p12f * r : r;
 }
 
+// Asks for kernel arguments in scalar registers at this point, in one statement. Placed at the top
+// of a kernel with every pointer the kernel dereferences and the sizes that decide its branches, it
+// makes the compiler issue all of the argument loads together and wait for them once; left to
+// itself, it loads the pointers used inside a branch only after waiting for the values that decide
+// the branch, a second dependent round trip before the first data load (measured: 2-3 % of a
+// decode-sized call). All kMaxInputs input pointers are named, used or not: they come in the same
+// argument block. The split-row kernels do without: there it measured slower (their combine reads
+// no input pointers and waits on the slice partials anyway).
+__device__ __forceinline__ void args_in_sgprs(const u32x4 *const (&in)[kMaxInputs], const void *p0,
+                                              const void *p1, const void *p2, uint32_t u0, uint32_t u1)
+{
+    asm volatile("" ::"s"(in[0]), "s"(in[1]), "s"(in[2]), "s"(in[3]), "s"(in[4]), "s"(in[5]),
+                 "s"(in[6]), "s"(in[7]), "s"(p0), "s"(p1), "s"(p2), "s"(u0), "s"(u1));
+}
+
 // A pack at a byte offset from a wave-uniform base (the base stays in scalar registers, the
 // per-lane offset is 32 bits). load_pack is an ordinary load (the weight, read by every row, and
 // inputs that may still be cached); load_stream is a non-temporal load (inputs streamed from HBM,
@@ -154,6 +169,7 @@ __global__ void __launch_bounds__(1024) k_rows(RowArgs a)
 {
     static_assert(kResidual || N == 1, "the plain RMSNorm reads one input");
     __shared__ float slots[kMaxWaves];
+    args_in_sgprs(a.in, a.residual, a.weight, a.residual_out, (uint32_t)a.packs, blockDim.x);
     const uint32_t tid = threadIdx.x;
     const uint32_t nthreads = blockDim.x;
     const uint32_t packs = (uint32_t)a.packs;
@@ -228,6 +244,7 @@ __global__ void __launch_bounds__(1024) k_rows(RowArgs a)
 template <int N, bool kStream>
 __global__ void __launch_bounds__(1024) k_flat_reduce(FlatArgs a)
 {
+    args_in_sgprs(a.in, a.out, a.out, a.out, a.packs, blockDim.x);
     const uint32_t first = blockIdx.x * blockDim.x;
     if (first + threadIdx.x >= a.packs)
         return;
