@@ -475,6 +475,7 @@ int execute(const Plan &plan, const fa_bf16 *const *inputs, int n, const fa_bf16
     a.eps = eps;
     a.inv_hidden = static_cast<float>(1.0 / hidden);
     a.packs = packs;
+    a.tiny_eps = eps < 0x1p-126f;
 
     if (plan.path == FUSED_AR_PATH_ONESTAGE) {
         for (int i = 0; i < n; ++i)
@@ -668,6 +669,7 @@ extern "C" int fused_ar_rmsnorm_split(const fa_bf16 *const *inputs, int n, const
         a.r.eps = eps;
         a.r.inv_hidden = static_cast<float>(1.0 / hidden);
         a.r.packs = packs;
+        a.r.tiny_eps = eps < 0x1p-126f;
         a.partial = static_cast<float *>(workspace) + (size_t)first * (size_t)s;
         a.splits = s;
         a.slice_packs = slice_packs;

@@ -38,6 +38,7 @@ struct RowArgs {
     float eps;
     float inv_hidden;             // 1 / hidden rounded to fp32: the mean is the square-sum times it
     int packs;                    // packs per row = hidden / 8
+    int tiny_eps;                 // eps < 2^-126: mean + eps may be subnormal (see rsqrt_f32)
 };
 
 struct FlatArgs {
@@ -89,11 +90,15 @@ __device__ __forceinline__ u32x4 normalise(const F8 &y, const F8 &g, float rstd)
     return narrow(o);
 }
 
-// 1 / sqrt(v) for v >= 0 by the hardware reciprocal square root (v_rsq_f32, within 1 ulp in
-// fp32). Below the normal range v is scaled by 2^24 first (and the result by 2^12), so subnormal
-// arguments, possible only with eps = 0 or eps subnormal, keep the same accuracy; 0 gives +inf.
-__device__ __forceinline__ float rsqrt_f32(float v)
+// 1 / sqrt(v) for v = mean + eps >= eps by the hardware reciprocal square root (v_rsq_f32, within
+// 1 ulp in fp32). Below the normal range v is scaled by 2^24 first (and the result by 2^12), so
+// subnormal arguments keep the same accuracy; 0 gives +inf. They are possible only when eps itself
+// is below the normal range (eps = 0 or subnormal), which the host flags: otherwise the scaling is
+// left out of the row's path (a uniform branch).
+__device__ __forceinline__ float rsqrt_f32(float v, int tiny_eps)
 {
+    if (!tiny_eps)
+        return __builtin_amdgcn_rsqf(v);
     const bool tiny = v < 0x1p-126f;
     const float r = __builtin_amdgcn_rsqf(tiny ? v * 0x1p24f : v);
     return tiny ? 0x1p12f * r : r;
@@ -108,10 +113,23 @@ __device__ __forceinline__ float rsqrt_f32(float v)
 // argument block. The split-row kernels do without: there it measured slower (their combine reads
 // no input pointers and waits on the slice partials anyway).
 __device__ __forceinline__ void args_in_sgprs(const u32x4 *const (&in)[kMaxInputs], const void *p0,
-                                              const void *p1, const void *p2, uint32_t u0, uint32_t u1)
+                                              uint32_t u0, uint32_t u1)
 {
     asm volatile("" ::"s"(in[0]), "s"(in[1]), "s"(in[2]), "s"(in[3]), "s"(in[4]), "s"(in[5]),
-                 "s"(in[6]), "s"(in[7]), "s"(p0), "s"(p1), "s"(p2), "s"(u0), "s"(u1));
+                 "s"(in[6]), "s"(in[7]), "s"(p0), "s"(u0), "s"(u1));
+}
+
+// The same for the row kernel, which also keeps the row statistic's arguments: named as outputs
+// of the statement they count as values it produced, so the compiler holds them in registers
+// instead of loading them from the argument block again after the barrier.
+__device__ __forceinline__ void args_in_sgprs(const RowArgs &a, float &eps, float &inv_hidden,
+                                              int &tiny_eps)
+{
+    asm volatile(""
+                 : "+s"(eps), "+s"(inv_hidden), "+s"(tiny_eps)
+                 : "s"(a.in[0]), "s"(a.in[1]), "s"(a.in[2]), "s"(a.in[3]), "s"(a.in[4]),
+                   "s"(a.in[5]), "s"(a.in[6]), "s"(a.in[7]), "s"(a.residual), "s"(a.weight),
+                   "s"(a.residual_out), "s"(a.out), "s"(a.packs), "s"(blockDim.x));
 }
 
 // A pack at a byte offset from a wave-uniform base (the base stays in scalar registers, the
@@ -169,7 +187,9 @@ __global__ void __launch_bounds__(1024) k_rows(RowArgs a)
 {
     static_assert(kResidual || N == 1, "the plain RMSNorm reads one input");
     __shared__ float slots[kMaxWaves];
-    args_in_sgprs(a.in, a.residual, a.weight, a.residual_out, (uint32_t)a.packs, blockDim.x);
+    float eps = a.eps, inv_hidden = a.inv_hidden;
+    int tiny_eps = a.tiny_eps;
+    args_in_sgprs(a, eps, inv_hidden, tiny_eps);
     const uint32_t tid = threadIdx.x;
     const uint32_t nthreads = blockDim.x;
     const uint32_t packs = (uint32_t)a.packs;
@@ -220,7 +240,7 @@ __global__ void __launch_bounds__(1024) k_rows(RowArgs a)
     }
 
     const float total = block_sum<kBpermute>(ss, slots);
-    const float rstd = rsqrt_f32(total * a.inv_hidden + a.eps);
+    const float rstd = rsqrt_f32(total * inv_hidden + eps, tiny_eps);
 
 #pragma unroll
     for (int k = 0; k < PPT; ++k) {
@@ -244,7 +264,7 @@ __global__ void __launch_bounds__(1024) k_rows(RowArgs a)
 template <int N, bool kStream>
 __global__ void __launch_bounds__(1024) k_flat_reduce(FlatArgs a)
 {
-    args_in_sgprs(a.in, a.out, a.out, a.out, a.packs, blockDim.x);
+    args_in_sgprs(a.in, a.out, a.packs, blockDim.x);
     const uint32_t first = blockIdx.x * blockDim.x;
     if (first + threadIdx.x >= a.packs)
         return;
@@ -314,7 +334,7 @@ __global__ void __launch_bounds__(1024) k_split_norm(SplitArgs a)
     float total = part[0];
     for (uint32_t i = 1; i < splits; ++i)
         total = total + part[i];
-    const float rstd = rsqrt_f32(total * a.r.inv_hidden + a.r.eps);
+    const float rstd = rsqrt_f32(total * a.r.inv_hidden + a.r.eps, a.r.tiny_eps);
     if (threadIdx.x < (uint32_t)a.slice_packs && p < packs) {
         const uint32_t off = p * (uint32_t)sizeof(u32x4);
         const F8 y = widen(load_pack(reinterpret_cast<const char *>(a.r.residual_out) + row_bytes, off));
