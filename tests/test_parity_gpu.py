@@ -243,11 +243,12 @@ def test_eps_values(eps):
         check_problem(p, path)
 
 
-@pytest.mark.parametrize("eps", [0.0, 1e-44])
+@pytest.mark.parametrize("eps", [0.0, 1e-44, 2.0 ** -126])
 def test_tiny_rows_with_subnormal_mean_square(eps):
     """Rows scaled by 2^-60 .. 2^-68, so that mean(x^2) + eps falls from the normal range (1e-36)
     into fp32's subnormals (down to 3e-41) with eps = 0 or subnormal: the reciprocal square root
-    must stay accurate there."""
+    must stay accurate there. With eps = 2^-126, the smallest normal value, mean + eps stays normal
+    although the mean is subnormal, and the kernel takes its unscaled form."""
     rng = np.random.default_rng(31)
     scales = [2.0 ** -60, 2.0 ** -63, 2.0 ** -66, 2.0 ** -68]
     inputs = [synth.to_bf16_bits(np.array([rng.standard_normal(64) * s for s in scales],
