@@ -324,23 +324,37 @@ __global__ void __launch_bounds__(1024) k_split_reduce(SplitArgs a)
 
 __global__ void __launch_bounds__(1024) k_split_norm(SplitArgs a)
 {
+    // this kernel's arguments in one scalar round trip (see args_in_sgprs)
+    asm volatile("" ::"s"(a.partial), "s"(a.r.residual_out), "s"(a.r.weight), "s"(a.r.out),
+                 "s"(a.splits), "s"(a.slice_packs), "s"(a.r.packs), "s"(blockDim.x));
     const uint32_t splits = (uint32_t)a.splits;
     const uint32_t row = blockIdx.x / splits;
     const uint32_t slice = blockIdx.x - row * splits;
     const uint32_t packs = (uint32_t)a.r.packs;
     const uint32_t p = slice * (uint32_t)a.slice_packs + threadIdx.x;
     const size_t row_bytes = (size_t)row * packs * sizeof(u32x4);
-    const float *part = a.partial + (size_t)row * splits;
-    float total = part[0];
-    for (uint32_t i = 1; i < splits; ++i)
-        total = total + part[i];
-    const float rstd = rsqrt_f32(total * a.r.inv_hidden + a.r.eps, a.r.tiny_eps);
-    if (threadIdx.x < (uint32_t)a.slice_packs && p < packs) {
-        const uint32_t off = p * (uint32_t)sizeof(u32x4);
-        const F8 y = widen(load_pack(reinterpret_cast<const char *>(a.r.residual_out) + row_bytes, off));
-        const F8 g = widen(load_pack(reinterpret_cast<const char *>(a.r.weight), off));
-        store_stream(reinterpret_cast<char *>(a.r.out) + row_bytes, off, normalise(y, g, rstd));
+    const bool active = threadIdx.x < (uint32_t)a.slice_packs && p < packs;
+    const uint32_t off = p * (uint32_t)sizeof(u32x4);
+    // the slice's residual_out and weight do not depend on the row statistic: their loads go out
+    // first, so that their round trip overlaps the one for the square-sums
+    u32x4 yv = {0, 0, 0, 0}, gv = {0, 0, 0, 0};
+    if (active) {
+        yv = load_pack(reinterpret_cast<const char *>(a.r.residual_out) + row_bytes, off);
+        gv = load_pack(reinterpret_cast<const char *>(a.r.weight), off);
     }
+    // the row's slice square-sums (at most 64, and a workgroup is whole waves) are loaded at once,
+    // lane i taking slice i, then added in slice order from registers: one memory round trip
+    // instead of a load and a wait per slice
+    const float *part = a.partial + (size_t)row * splits;
+    const uint32_t lane = threadIdx.x & 63;
+    const float mine = lane < splits ? part[lane] : 0.0f;
+    float total = lane_value(mine, 0);
+    for (uint32_t i = 1; i < splits; ++i)
+        total = total + lane_value(mine, (int)i);
+    const float rstd = rsqrt_f32(total * a.r.inv_hidden + a.r.eps, a.r.tiny_eps);
+    if (active)
+        store_stream(reinterpret_cast<char *>(a.r.out) + row_bytes, off,
+                     normalise(widen(yv), widen(gv), rstd));
 }
 
 // Stage 1 with LDS staging, one wave per input (the one-wave-per-rank design that the flat reduce
