@@ -322,6 +322,43 @@ def test_rejects_aliasing_out_on_gpu_tensors():
     assert e.value.status == fa.ERR_ALIAS
 
 
+# ------------------------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("n,m,hidden", [(8, 37, 7168), (4, 300, 2880)])
+def test_row_permutation_equivariance(n, m, hidden, path):
+    """Rows are independent: permuting the rows of every input and of the residual permutes both
+    outputs, bit for bit (a mistake in the row indexing of any kernel fails this)."""
+    p = synth.make_problem(n, m, hidden, seed=41, name="rows")
+    perm = np.random.default_rng(41).permutation(m)
+    announce(f"row permutation n={n} m={m} hidden={hidden} path={path}")
+    ro, out = run_gpu(p, path)
+    q = synth.Problem([x[perm] for x in p.inputs], p.residual[perm], p.weight, p.eps)
+    ro_q, out_q = run_gpu(q, path)
+    assert np.array_equal(ro_q, ro[perm])
+    assert np.array_equal(out_q, out[perm])
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_input_order_irrelevant_when_sums_are_exact(path):
+    """Inputs that are multiples of 2^-4 with |value| <= 8 make every fp32 partial sum exact, so the
+    reduce result, and with it both outputs, cannot depend on the order of the inputs: reversing or
+    rotating them leaves the bits unchanged (an input dropped or read twice changes them)."""
+    rng = np.random.default_rng(43)
+    n, m, hidden = 8, 24, 7168
+    ins = [synth.to_bf16_bits(rng.integers(-128, 129, (m, hidden)).astype(np.float32) / 16)
+           for _ in range(n)]
+    residual = synth.to_bf16_bits(rng.standard_normal((m, hidden), dtype=np.float32))
+    weight = synth.to_bf16_bits((1 + 0.1 * rng.standard_normal(hidden)).astype(np.float32))
+    p = synth.Problem(ins, residual, weight, 1e-6, name="exact sums")
+    ro, out = check_problem(p, path)
+    for order in (ins[::-1], ins[3:] + ins[:3]):
+        announce(f"input order path={path}")
+        ro_q, out_q = run_gpu(synth.Problem(order, residual, weight, 1e-6), path)
+        assert np.array_equal(ro_q, ro)
+        assert np.array_equal(out_q, out)
+
+
 # ------------------------------------------------------------------------- repeatability
 
 def test_deterministic():
