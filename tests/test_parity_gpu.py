@@ -359,6 +359,27 @@ def test_input_order_irrelevant_when_sums_are_exact(path):
         assert np.array_equal(out_q, out)
 
 
+def _bf16_values(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).float().numpy()
+
+
+@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("k", [-20, 7])
+def test_power_of_two_scaling(k, path):
+    """Scaling every input and the residual by 2^k scales residual_out by exactly 2^k (fp32 sums
+    and the rounding to bf16 commute with it while nothing overflows or turns subnormal), and with
+    eps = 0 the normalised row is unchanged: out stays within the 1-ulp band of the unscaled call."""
+    p = synth.make_problem(8, 16, 7168, seed=47, eps=0.0, name="scale")
+    announce(f"power-of-two scaling k={k} path={path}")
+    ro, out = run_gpu(p, path)
+    s = np.float32(2.0 ** k)
+    q = synth.Problem([synth.to_bf16_bits(_bf16_values(x) * s) for x in p.inputs],
+                      synth.to_bf16_bits(_bf16_values(p.residual) * s), p.weight, 0.0)
+    ro_k, out_k = run_gpu(q, path)
+    assert np.array_equal(ro_k, synth.to_bf16_bits(_bf16_values(ro) * s))
+    assert ulp_diff(out_k, out).max() <= OUT_ULP
+
+
 # ------------------------------------------------------------------------- repeatability
 
 def test_deterministic():
