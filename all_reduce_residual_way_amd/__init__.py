@@ -20,7 +20,8 @@ __all__ = [
     "auto_path", "describe_launch", "strerror",
     "OK", "ERR_INVALID", "ERR_SHAPE", "ERR_ALIGN", "ERR_ALIAS",
     "PATH_AUTO", "PATH_ONESTAGE", "PATH_TWOSTAGE", "PATH_UNFUSED", "WAVE_DPP", "WAVE_BPERMUTE",
-    "STAGE1_FLAT", "STAGE1_LDS", "LOAD_AUTO", "LOAD_CACHED", "LOAD_STREAM", "MAX_INPUTS",
+    "STAGE1_FLAT", "STAGE1_LDS", "LOAD_AUTO", "LOAD_CACHED", "LOAD_STREAM", "CHUNKS_AUTO",
+    "CHUNKS_SEQUENTIAL", "CHUNKS_PIPELINED", "MAX_INPUTS",
     "MAX_HIDDEN",
 ]
 
@@ -32,6 +33,7 @@ PATH_AUTO, PATH_ONESTAGE, PATH_TWOSTAGE, PATH_UNFUSED = 0, 1, 2, 3
 WAVE_DPP, WAVE_BPERMUTE = 0, 1
 STAGE1_FLAT, STAGE1_LDS = 0, 1
 LOAD_AUTO, LOAD_CACHED, LOAD_STREAM = 0, 1, 2
+CHUNKS_AUTO, CHUNKS_SEQUENTIAL, CHUNKS_PIPELINED = 0, 1, 2
 MAX_INPUTS, MAX_HIDDEN = 8, 32768
 
 _VP = ctypes.c_void_p
@@ -51,7 +53,8 @@ class Options(ctypes.Structure):
     """fused_ar_options: alternative kernel designs (see include/fused_ar.h)."""
     _fields_ = [("wave_reduce", ctypes.c_int), ("stage1", ctypes.c_int),
                 ("stage1_block", ctypes.c_int), ("packs_per_thread", ctypes.c_int),
-                ("load_policy", ctypes.c_int)]
+                ("load_policy", ctypes.c_int), ("stage_rows", ctypes.c_int),
+                ("schedule", ctypes.c_int)]
 
 
 class FusedArError(RuntimeError):

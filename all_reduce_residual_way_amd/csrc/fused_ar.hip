@@ -110,9 +110,12 @@ struct Options {
     unsigned flat_block;  // workgroup of the flat kernels; 0 = by size (flat_block_for)
     int ppt;              // packs per thread of the row kernels; 0 = automatic
     int load_policy;      // FUSED_AR_LOAD_AUTO, _CACHED or _STREAM
+    int stage_rows;       // two-stage path: rows per chunk; 0 = automatic, -1 = one chunk
+    int schedule;         // FUSED_AR_CHUNKS_AUTO, _SEQUENTIAL or _PIPELINED
 };
 
-constexpr Options kDefaultOptions = {false, false, 0, 0, FUSED_AR_LOAD_AUTO};
+constexpr Options kDefaultOptions = {false, false, 0, 0, FUSED_AR_LOAD_AUTO, 0,
+                                     FUSED_AR_CHUNKS_AUTO};
 
 unsigned flat_block_for(const Options &o, size_t total_packs)
 {
@@ -153,11 +156,18 @@ int read_options(const fused_ar_options *o, Options *out)
     if (o->load_policy != FUSED_AR_LOAD_AUTO && o->load_policy != FUSED_AR_LOAD_CACHED &&
         o->load_policy != FUSED_AR_LOAD_STREAM)
         return FUSED_AR_ERR_INVALID;
+    if (o->stage_rows < -1 || o->stage_rows > kRowsPerLaunch)
+        return FUSED_AR_ERR_INVALID;
+    if (o->schedule != FUSED_AR_CHUNKS_AUTO && o->schedule != FUSED_AR_CHUNKS_SEQUENTIAL &&
+        o->schedule != FUSED_AR_CHUNKS_PIPELINED)
+        return FUSED_AR_ERR_INVALID;
     out->bpermute = o->wave_reduce == FUSED_AR_WAVE_BPERMUTE;
     out->lds_stage1 = o->stage1 == FUSED_AR_STAGE1_LDS;
     out->flat_block = static_cast<unsigned>(o->stage1_block);
     out->ppt = o->packs_per_thread;
     out->load_policy = o->load_policy;
+    out->stage_rows = o->stage_rows;
+    out->schedule = o->schedule;
     return FUSED_AR_OK;
 }
 
@@ -267,6 +277,38 @@ const void *flat_kernel(int n, bool stream)
     return stream ? flat_kernel_s<true>(n) : flat_kernel_s<false>(n);
 }
 
+template <int P, bool kS>
+const void *pipe_kernel_ps(int n)
+{
+    switch (n) {
+    case 1: return reinterpret_cast<const void *>(&fa::k_pipe<1, P, kS>);
+    case 2: return reinterpret_cast<const void *>(&fa::k_pipe<2, P, kS>);
+    case 3: return reinterpret_cast<const void *>(&fa::k_pipe<3, P, kS>);
+    case 4: return reinterpret_cast<const void *>(&fa::k_pipe<4, P, kS>);
+    case 5: return reinterpret_cast<const void *>(&fa::k_pipe<5, P, kS>);
+    case 6: return reinterpret_cast<const void *>(&fa::k_pipe<6, P, kS>);
+    case 7: return reinterpret_cast<const void *>(&fa::k_pipe<7, P, kS>);
+    case 8: return reinterpret_cast<const void *>(&fa::k_pipe<8, P, kS>);
+    default: return nullptr;
+    }
+}
+
+template <bool kS>
+const void *pipe_kernel_s(int n, int ppt)
+{
+    switch (ppt) {
+    case 1: return pipe_kernel_ps<1, kS>(n);
+    case 2: return pipe_kernel_ps<2, kS>(n);
+    case 4: return pipe_kernel_ps<4, kS>(n);
+    default: return nullptr;
+    }
+}
+
+const void *pipe_kernel(int n, int ppt, bool stream)
+{
+    return stream ? pipe_kernel_s<true>(n, ppt) : pipe_kernel_s<false>(n, ppt);
+}
+
 template <bool kS>
 const void *lds_kernel_s(int n)
 {
@@ -340,7 +382,30 @@ struct Plan {
     int path;  // FUSED_AR_PATH_ONESTAGE, FUSED_AR_PATH_TWOSTAGE or kPathUnfusedPlan
     int steps;
     Step step[3];
+    int chunk_rows;  // two-stage path: rows per chunk (m: one chunk)
+    bool pipelined;  // two-stage path in chunks: stage 2 of a chunk and stage 1 of the next share
+                     // a launch (k_pipe)
 };
+
+// Rows per chunk of the two-stage path, and whether the chunks are pipelined.
+int chunk_rows_for(const Options &o, int m)
+{
+    if (o.stage_rows == -1)
+        return m;
+    if (o.stage_rows > 0)
+        return o.stage_rows < m ? o.stage_rows : m;
+    return m;
+}
+
+bool pipelined_for(const Options &o)
+{
+    return o.schedule == FUSED_AR_CHUNKS_PIPELINED;
+}
+
+size_t flat_launches(size_t packs)
+{
+    return (packs + kFlatPacksPerLaunch - 1) / kFlatPacksPerLaunch;
+}
 
 // A flat kernel over total_packs packs, one per thread, in launches of at most
 // kFlatPacksPerLaunch packs; `grid` is that of the first launch.
@@ -392,8 +457,48 @@ int make_plan(int n, int m, int hidden, int path, const Options &o, Plan *plan)
     if (path == FUSED_AR_PATH_TWOSTAGE) {
         rows.kernel = row_kernel(1, ppt, o.bpermute, true, stream);
         rows.name = "stage2_norm";
+        const int r = chunk_rows_for(o, m);
+        plan->chunk_rows = r;
         plan->steps = 2;
-        plan->step[1] = rows;
+        if (r == m) {
+            plan->step[1] = rows;
+            return FUSED_AR_OK;
+        }
+        // chunks of r <= kRowsPerLaunch rows: one row launch per chunk
+        const int64_t chunks = ((int64_t)m + r - 1) / r;
+        const int last = static_cast<int>(m - (chunks - 1) * r);
+        const size_t chunk_packs = (size_t)r * (size_t)packs;
+        const size_t last_packs = (size_t)last * (size_t)packs;
+        if (o.lds_stage1)
+            plan->step[0] = flat_step(lds_kernel(n, stream), "stage1_reduce_lds", n, chunk_packs,
+                                      64u * static_cast<unsigned>(n), stream);
+        else
+            plan->step[0] = flat_step(flat_kernel(n, stream), "stage1_reduce", n, chunk_packs,
+                                      flat_block_for(o, chunk_packs), stream);
+        rows.grid = static_cast<unsigned>(r);
+        if (!pipelined_for(o)) {
+            // stage 1 then stage 2 on each chunk in turn
+            plan->step[0].launches = static_cast<unsigned>(
+                (size_t)(chunks - 1) * flat_launches(chunk_packs) + flat_launches(last_packs));
+            rows.launches = static_cast<unsigned>(chunks);
+            plan->step[1] = rows;
+            return FUSED_AR_OK;
+        }
+        // stage 1 of the first chunk; chunks - 1 launches of stage 2 of chunk c with stage 1 of
+        // chunk c + 1; stage 2 of the last chunk
+        plan->pipelined = true;
+        plan->step[0].launches = static_cast<unsigned>(flat_launches(chunk_packs));
+        Step pipe = rows;
+        pipe.kernel = pipe_kernel(n, ppt, stream);
+        pipe.name = "stage_pipe";
+        pipe.n = n;
+        pipe.grid = static_cast<unsigned>(r + (chunks == 2 ? last : r));
+        pipe.launches = static_cast<unsigned>(chunks - 1);
+        plan->step[1] = pipe;
+        rows.grid = static_cast<unsigned>(last);
+        rows.launches = 1;
+        plan->step[2] = rows;
+        plan->steps = 3;
         return FUSED_AR_OK;
     }
     // unfused: the residual add is the flat reduce of (reduced, residual); then a plain RMSNorm
@@ -454,6 +559,75 @@ int run_flat(const Step &s, const u32x4 *const *inputs, size_t total_packs, u32x
     return FUSED_AR_OK;
 }
 
+// The two-stage path in chunks of plan.chunk_rows rows (fewer than m). `a` holds the call's
+// buffers at row 0; each chunk's stage 1 writes its reduced rows into `out`, and its stage 2 reads
+// them back and overwrites them with the normalised rows. Sequential: stage 1 and stage 2 of each
+// chunk in turn. Pipelined: stage 1 of the first chunk, then launches of stage 2 of chunk c
+// together with stage 1 of chunk c + 1, then stage 2 of the last chunk.
+int run_chunks(const Plan &plan, const u32x4 *const *ins, int n, const RowArgs &a, int m,
+               int packs, hipStream_t stream)
+{
+    const int64_t r = plan.chunk_rows;
+    // the call's buffers moved to row `first`, stage 2 reading the reduced rows from `out`
+    auto at_row = [&](int64_t first) {
+        const size_t skip = (size_t)first * (size_t)packs;
+        RowArgs c = a;
+        c.in[0] = a.out + skip;
+        for (int i = 1; i < fa::kMaxInputs; ++i)
+            c.in[i] = nullptr;
+        c.residual += skip;
+        c.residual_out += skip;
+        c.out += skip;
+        return c;
+    };
+    auto stage1 = [&](int64_t first, int64_t rows) {
+        const size_t skip = (size_t)first * (size_t)packs;
+        const u32x4 *chunk_in[FUSED_AR_MAX_INPUTS];
+        for (int i = 0; i < n; ++i)
+            chunk_in[i] = ins[i] + skip;
+        return run_flat(plan.step[0], chunk_in, (size_t)rows * (size_t)packs, a.out + skip,
+                        stream);
+    };
+    const Step &norm = plan.pipelined ? plan.step[2] : plan.step[1];
+    auto stage2 = [&](int64_t first, int64_t rows) {
+        RowArgs c = at_row(first);
+        return launch(norm.kernel, static_cast<unsigned>(rows), norm.block, &c, stream, norm.lds);
+    };
+    if (!plan.pipelined) {
+        for (int64_t first = 0; first < m; first += r) {
+            const int64_t rows = m - first < r ? m - first : r;
+            int rc = stage1(first, rows);
+            if (rc == FUSED_AR_OK)
+                rc = stage2(first, rows);
+            if (rc != FUSED_AR_OK)
+                return rc;
+        }
+        return FUSED_AR_OK;
+    }
+    int rc = stage1(0, r);
+    if (rc != FUSED_AR_OK)
+        return rc;
+    const Step &pipe = plan.step[1];
+    int64_t first = 0;  // the chunk whose stage 2 is next
+    for (; first + r < m; first += r) {
+        const int64_t next = first + r;
+        const int64_t next_rows = m - next < r ? m - next : r;
+        fa::PipeArgs p{};
+        p.norm = at_row(first);
+        const size_t skip = (size_t)next * (size_t)packs;
+        for (int i = 0; i < n; ++i)
+            p.reduce.in[i] = ins[i] + skip;
+        p.reduce.out = a.out + skip;
+        p.reduce.packs = static_cast<uint32_t>(packs);
+        p.norm_rows = static_cast<uint32_t>(r);
+        rc = launch(pipe.kernel, static_cast<unsigned>(r + next_rows), pipe.block, &p, stream,
+                    pipe.lds);
+        if (rc != FUSED_AR_OK)
+            return rc;
+    }
+    return stage2(first, m - first);
+}
+
 // Runs a validated call (m > 0) along `plan`.
 int execute(const Plan &plan, const fa_bf16 *const *inputs, int n, const fa_bf16 *residual,
             const fa_bf16 *weight, float eps, int m, int hidden, fa_bf16 *residual_out,
@@ -482,6 +656,8 @@ int execute(const Plan &plan, const fa_bf16 *const *inputs, int n, const fa_bf16
             a.in[i] = ins[i];
         return run_rows(plan.step[0], a, m, packs, stream);
     }
+    if (plan.path == FUSED_AR_PATH_TWOSTAGE && plan.chunk_rows < m)
+        return run_chunks(plan, ins, n, a, m, packs, stream);
     // Two-stage and unfused: the reduce writes the reduced rows into `out`.
     int rc = run_flat(plan.step[0], ins, total, o, stream);
     if (rc != FUSED_AR_OK)

@@ -10,6 +10,8 @@
 //   k_split_reduce<N>, k_split_norm
 //                      split rows: the one-stage result with each row cut into slices on separate
 //                      workgroups, the second kernel combining the slices' square-sums.
+//   k_pipe<N, PPT>     the two-stage path in row chunks: stage 2 of one chunk and stage 1 of the
+//                      next in one launch.
 //   k_stage1_lds<N>    the LDS-staged, one-wave-per-input stage 1 that the flat reduce replaced,
 //                      kept for comparison.
 //
@@ -169,9 +171,10 @@ __device__ __forceinline__ u32x4 load_once(const char *base, uint32_t off)
         return load_pack(base, off);
 }
 
-// Workgroup b handles row b (the host launches one workgroup per row, splitting very tall
-// problems into several launches); thread t handles packs t, t + blockDim.x, ..., PPT of them.
-// For each of its packs a thread loads the N inputs, the residual and the weight, reduces,
+// One row of the row kernel (k_rows: workgroup b handles row b; the host launches one workgroup
+// per row, splitting very tall problems into several launches); thread t handles packs t,
+// t + blockDim.x, ..., PPT of them. `eps`, `inv_hidden` and `tiny_eps` are the caller's copies of
+// the argument fields (see args_in_sgprs). For each of its packs a thread loads the N inputs, the residual and the weight, reduces,
 // writes residual_out and accumulates the square-sum, keeping only the bf16 residual_out and
 // weight packs; one workgroup reduction then gives the row statistic and the normalised row is
 // written from those registers.
@@ -183,17 +186,14 @@ __device__ __forceinline__ u32x4 load_once(const char *base, uint32_t off)
 //              input is the reduced rows the flat reduce has just stored (two-stage path, unfused
 //              sequence), which may still be in the Infinity Cache, so it is always loaded normally.
 template <int N, int PPT, bool kBpermute, bool kResidual, bool kStream>
-__global__ void __launch_bounds__(1024) k_rows(RowArgs a)
+__device__ __forceinline__ void row_pass(const RowArgs &a, float eps, float inv_hidden,
+                                         int tiny_eps, uint32_t row, float *slots)
 {
     static_assert(kResidual || N == 1, "the plain RMSNorm reads one input");
-    __shared__ float slots[kMaxWaves];
-    float eps = a.eps, inv_hidden = a.inv_hidden;
-    int tiny_eps = a.tiny_eps;
-    args_in_sgprs(a, eps, inv_hidden, tiny_eps);
     const uint32_t tid = threadIdx.x;
     const uint32_t nthreads = blockDim.x;
     const uint32_t packs = (uint32_t)a.packs;
-    const size_t row_bytes = (size_t)blockIdx.x * packs * sizeof(u32x4);
+    const size_t row_bytes = (size_t)row * packs * sizeof(u32x4);
     const char *weight = reinterpret_cast<const char *>(a.weight);
     const char *in[N];
 #pragma unroll
@@ -259,6 +259,17 @@ __global__ void __launch_bounds__(1024) k_rows(RowArgs a)
     }
 }
 
+template <int N, int PPT, bool kBpermute, bool kResidual, bool kStream>
+__global__ void __launch_bounds__(1024) k_rows(RowArgs a)
+{
+    __shared__ float slots[kMaxWaves];
+    float eps = a.eps, inv_hidden = a.inv_hidden;
+    int tiny_eps = a.tiny_eps;
+    args_in_sgprs(a, eps, inv_hidden, tiny_eps);
+    row_pass<N, PPT, kBpermute, kResidual, kStream>(a, eps, inv_hidden, tiny_eps, blockIdx.x,
+                                                     slots);
+}
+
 // Flat N-way reduce: thread t of workgroup b handles pack b * blockDim.x + t (one pack per thread;
 // the host launches enough workgroups, splitting more than 2^30 packs into several launches).
 template <int N, bool kStream>
@@ -278,6 +289,54 @@ __global__ void __launch_bounds__(1024) k_flat_reduce(FlatArgs a)
     // the reduced rows are read straight back by the next kernel: an ordinary store, so that they
     // can stay in the Infinity Cache
     store_pack(reinterpret_cast<char *>(a.out) + bytes, off, narrow(reduce_packs<N>(x)));
+}
+
+// Two-stage path in row chunks, pipelined: one launch runs stage 2 on the rows of one chunk,
+// whose reduced rows the previous launch stored into `out`, and stage 1 on the rows of the next
+// chunk. The launch boundary orders the two stages of a chunk; within a launch the two kinds of
+// workgroup touch disjoint rows. Workgroups [0, norm_rows) take stage 2 (the row kernel's pass
+// with one input, the call's geometry, so `out` is bit-identical to the other paths); workgroups
+// [norm_rows, norm_rows + reduce_rows) take stage 1 of one row each (thread t reduces packs
+// t, t + blockDim.x, ... of the row, the same per-pack arithmetic as k_flat_reduce).
+struct PipeArgs {
+    RowArgs norm;     // stage 2: in[0] = the reduced rows of the chunk (in `out`), other buffers
+                      // at the same chunk's first row
+    FlatArgs reduce;  // stage 1: in[0..N-1] and out (the scratch) at the next chunk's first row;
+                      // `packs` is the row length here
+    uint32_t norm_rows;
+};
+
+// Stage 1 of one row: the N-way reduce of each of the thread's packs, stored into the scratch.
+template <int N, int PPT, bool kStream>
+__device__ __forceinline__ void reduce_row(const FlatArgs &f, uint32_t row)
+{
+    const uint32_t packs = f.packs;
+    const size_t row_bytes = (size_t)row * packs * sizeof(u32x4);
+    char *dst = reinterpret_cast<char *>(f.out) + row_bytes;
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+        const uint32_t p = threadIdx.x + k * blockDim.x;
+        if (p < packs) {
+            const uint32_t off = p * (uint32_t)sizeof(u32x4);
+            u32x4 x[N];
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+                x[i] = load_once<kStream>(reinterpret_cast<const char *>(f.in[i]) + row_bytes, off);
+            __builtin_amdgcn_sched_barrier(0);
+            store_pack(dst, off, narrow(reduce_packs<N>(x)));
+        }
+    }
+}
+
+template <int N, int PPT, bool kStream>
+__global__ void __launch_bounds__(1024) k_pipe(PipeArgs a)
+{
+    __shared__ float slots[kMaxWaves];
+    if (blockIdx.x < a.norm_rows)
+        row_pass<1, PPT, false, true, kStream>(a.norm, a.norm.eps, a.norm.inv_hidden,
+                                               a.norm.tiny_eps, blockIdx.x, slots);
+    else
+        reduce_row<N, PPT, kStream>(a.reduce, blockIdx.x - a.norm_rows);
 }
 
 // Split rows: each row is cut into `splits` slices of slice_packs packs, one workgroup per slice,

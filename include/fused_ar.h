@@ -158,6 +158,19 @@ enum {
     FUSED_AR_LOAD_STREAM = 2   /* always non-temporal loads */
 };
 
+/* How the two-stage path runs when it is cut into chunks of rows (fused_ar_options.stage_rows):
+ * each chunk's stage 1 stores its reduced rows into `out` and its stage 2 reads them back soon
+ * after, while they may still be in the L2s or the Infinity Cache, instead of after the whole
+ * call's stage 1. */
+enum {
+    FUSED_AR_CHUNKS_AUTO = 0,        /* the library's choice */
+    FUSED_AR_CHUNKS_SEQUENTIAL = 1,  /* stage 1 then stage 2 of each chunk in turn (two launches
+                                        per chunk) */
+    FUSED_AR_CHUNKS_PIPELINED = 2    /* one launch per chunk boundary: stage 2 of chunk c and
+                                        stage 1 of chunk c + 1 on separate workgroups of one
+                                        launch */
+};
+
 typedef struct {
     int wave_reduce;       /* FUSED_AR_WAVE_DPP or FUSED_AR_WAVE_BPERMUTE */
     int stage1;            /* FUSED_AR_STAGE1_FLAT or FUSED_AR_STAGE1_LDS */
@@ -170,6 +183,10 @@ typedef struct {
                               the inputs and the residual are loaded; streaming calls of more than
                               1024 rows also cap the row workgroups per CU and pick their packs
                               per thread (see fused_ar_rmsnorm_ex for what that does to `out`) */
+    int stage_rows;        /* two-stage path: rows per chunk, 1..2^20; 0 = automatic; -1 = the
+                              whole call as one chunk */
+    int schedule;          /* two-stage path in chunks: FUSED_AR_CHUNKS_AUTO, _SEQUENTIAL or
+                              _PIPELINED */
 } fused_ar_options;
 
 /*
@@ -223,6 +240,7 @@ int fused_ar_auto_path(int n, int m, int hidden);
 /* One kernel launch of a call, as fused_ar_describe_launch reports it. */
 typedef struct {
     char name[32];        /* kernel name: "onestage", "stage1_reduce", "stage1_reduce_lds",
+                             "stage_pipe" (stage 2 of one chunk with stage 1 of the next),
                              "stage2_norm", "residual_add" or "rmsnorm" */
     unsigned grid;        /* workgroups per launch (the row kernels: one per row) */
     unsigned block;       /* threads per workgroup (a multiple of 64) */

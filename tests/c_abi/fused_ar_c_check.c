@@ -44,7 +44,8 @@ static int cpu_checks(void)
           plan.launch[0].lds_bytes == 64u * 1024u); /* a long streaming call: two packs per thread */
     CHECK(fused_ar_describe_launch(8, 4096, 7168, FUSED_AR_PATH_UNFUSED, &plan) == FUSED_AR_OK);
     CHECK(plan.kernels == 3 && strcmp(plan.launch[2].name, "rmsnorm") == 0);
-    fused_ar_options opt = {FUSED_AR_WAVE_BPERMUTE, FUSED_AR_STAGE1_LDS, 0, 0, FUSED_AR_LOAD_AUTO};
+    fused_ar_options opt = {FUSED_AR_WAVE_BPERMUTE, FUSED_AR_STAGE1_LDS, 0, 0, FUSED_AR_LOAD_AUTO, 0,
+                            FUSED_AR_CHUNKS_AUTO};
     CHECK(fused_ar_describe_launch_ex(4, 64, 7168, FUSED_AR_PATH_TWOSTAGE, &opt, &plan) == FUSED_AR_OK);
     CHECK(strcmp(plan.launch[0].name, "stage1_reduce_lds") == 0 && plan.launch[0].block == 256);
 
@@ -70,7 +71,8 @@ static int cpu_checks(void)
        workgroups at this size */
     CHECK(plan.launch[0].launches == 8192u && plan.launch[0].grid == (1u << 21) &&
           plan.launch[0].block == 512u && plan.launch[0].per_thread == 1u);
-    fused_ar_options lds = {FUSED_AR_WAVE_DPP, FUSED_AR_STAGE1_LDS, 0, 0, FUSED_AR_LOAD_STREAM};
+    fused_ar_options lds = {FUSED_AR_WAVE_DPP, FUSED_AR_STAGE1_LDS, 0, 0, FUSED_AR_LOAD_STREAM, 0,
+                            FUSED_AR_CHUNKS_AUTO};
     CHECK(fused_ar_describe_launch_ex(8, 2147483647, 32768, FUSED_AR_PATH_TWOSTAGE, &lds, &plan) ==
           FUSED_AR_OK);
     CHECK(plan.launch[0].launches == 8192u && plan.launch[0].grid == (1u << 21));
@@ -105,8 +107,25 @@ static int cpu_checks(void)
           FUSED_AR_ERR_ALIAS);
     CHECK(fused_ar_reduce(ins, 3, 2147483647, 2147483640,
                           (fa_bf16 *)(uintptr_t)0xFFFF000000000000u, NULL) == FUSED_AR_ERR_INVALID);
-    fused_ar_options bad = {0, 0, 96, 0, 0};
-    fused_ar_options bad_policy = {0, 0, 0, 0, 3};
+    fused_ar_options bad = {0, 0, 96, 0, 0, 0, 0};
+    fused_ar_options bad_policy = {0, 0, 0, 0, 3, 0, 0};
+    fused_ar_options bad_rows = {0, 0, 0, 0, 0, (1 << 20) + 1, 0};
+    fused_ar_options bad_schedule = {0, 0, 0, 0, 0, 0, 3};
+    CHECK(fused_ar_describe_launch_ex(8, 64, 7168, 2, &bad_rows, &plan) == FUSED_AR_ERR_INVALID);
+    CHECK(fused_ar_describe_launch_ex(8, 64, 7168, 2, &bad_schedule, &plan) == FUSED_AR_ERR_INVALID);
+    /* the two-stage path in chunks of one row at the largest m: no overflow in the chunk count */
+    fused_ar_options one_row = {0, 0, 0, 0, 0, 1, FUSED_AR_CHUNKS_SEQUENTIAL};
+    CHECK(fused_ar_describe_launch_ex(8, 2147483647, 32768, 2, &one_row, &plan) == FUSED_AR_OK);
+    CHECK(plan.kernels == 2 && plan.launch[0].launches == 2147483647u &&
+          plan.launch[1].launches == 2147483647u && plan.launch[1].grid == 1u);
+    one_row.schedule = FUSED_AR_CHUNKS_PIPELINED;
+    CHECK(fused_ar_describe_launch_ex(8, 2147483647, 32768, 2, &one_row, &plan) == FUSED_AR_OK);
+    CHECK(plan.kernels == 3 && strcmp(plan.launch[1].name, "stage_pipe") == 0 &&
+          plan.launch[1].launches == 2147483646u && plan.launch[1].grid == 2u);
+    fused_ar_options big_rows = {0, 0, 0, 0, 0, 1 << 20, FUSED_AR_CHUNKS_SEQUENTIAL};
+    CHECK(fused_ar_describe_launch_ex(8, 2147483647, 32768, 2, &big_rows, &plan) == FUSED_AR_OK);
+    /* 2048 chunks of 2^20 rows (the last one row short) of 2^32 packs: four flat launches each */
+    CHECK(plan.launch[0].launches == 2048u * 4u && plan.launch[1].launches == 2048u);
     CHECK(fused_ar_rmsnorm_ex(ins, 3, fake(3), fake(4), 1e-6f, 8, 4096, (fa_bf16 *)fake(5),
                               (fa_bf16 *)fake(6), 1, &bad, NULL) == FUSED_AR_ERR_INVALID);
     CHECK(fused_ar_rmsnorm_ex(ins, 3, fake(3), fake(4), 1e-6f, 8, 4096, (fa_bf16 *)fake(5),

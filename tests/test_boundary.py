@@ -53,7 +53,10 @@ def test_header_constants_match_binding():
                         ("FUSED_AR_WAVE_DPP", fa.WAVE_DPP), ("FUSED_AR_WAVE_BPERMUTE", fa.WAVE_BPERMUTE),
                         ("FUSED_AR_STAGE1_FLAT", fa.STAGE1_FLAT), ("FUSED_AR_STAGE1_LDS", fa.STAGE1_LDS),
                         ("FUSED_AR_LOAD_AUTO", fa.LOAD_AUTO), ("FUSED_AR_LOAD_CACHED", fa.LOAD_CACHED),
-                        ("FUSED_AR_LOAD_STREAM", fa.LOAD_STREAM)]:
+                        ("FUSED_AR_LOAD_STREAM", fa.LOAD_STREAM),
+                        ("FUSED_AR_CHUNKS_AUTO", fa.CHUNKS_AUTO),
+                        ("FUSED_AR_CHUNKS_SEQUENTIAL", fa.CHUNKS_SEQUENTIAL),
+                        ("FUSED_AR_CHUNKS_PIPELINED", fa.CHUNKS_PIPELINED)]:
         assert re.search(rf"\b{name}\s*=\s*{value}\b", text), name
     assert re.search(rf"#define FUSED_AR_MAX_INPUTS {fa.MAX_INPUTS}\b", text)
     assert re.search(rf"#define FUSED_AR_MAX_HIDDEN {fa.MAX_HIDDEN}\b", text)
@@ -239,7 +242,8 @@ def test_options_struct_matches_header():
     fa.Options(2, 0, 0, 0), fa.Options(-1, 0, 0, 0), fa.Options(0, 2, 0, 0),
     fa.Options(0, 0, 32, 0), fa.Options(0, 0, 100, 0), fa.Options(0, 0, 2048, 0),
     fa.Options(0, 0, 0, 3), fa.Options(0, 0, 0, 8), fa.Options(0, 0, 0, 0, 3),
-    fa.Options(0, 0, 0, 0, -1)])
+    fa.Options(0, 0, 0, 0, -1), fa.Options(0, 0, 0, 0, 0, -2), fa.Options(0, 0, 0, 0, 0, (1 << 20) + 1),
+    fa.Options(0, 0, 0, 0, 0, 0, 3), fa.Options(0, 0, 0, 0, 0, 0, -1)])
 def test_bad_options_rejected_before_launch(opts):
     ins = [addr(i) for i in range(4)]
     rc = fa.fused_ar_rmsnorm_ex_ptrs(ins, addr(10), addr(11), 1e-6, 8, 4096, addr(12), addr(13),
@@ -261,6 +265,34 @@ def test_option_plans():
     with pytest.raises(fa.FusedArError) as e:
         fa.describe_launch(8, 100, 16384, 1, fa.Options(0, 0, 0, 1))
     assert e.value.status == fa.ERR_SHAPE
+
+
+def test_chunked_two_stage_plans():
+    """The two-stage path in chunks of rows: per chunk a flat reduce and a row launch
+    (sequential), or the first chunk's reduce, one launch per chunk boundary, the last chunk's
+    normalisation (pipelined). The one-stage path ignores the chunk options."""
+    def plan(m, rows, schedule, n=4, hidden=7168, path=2):
+        ks = fa.describe_launch(n, m, hidden, path,
+                                fa.Options(0, 0, 0, 0, 0, rows, schedule))["kernels"]
+        return [(k["name"], k["grid"], k["block"], k["per_thread"], k["launches"]) for k in ks]
+    seq, pipe = fa.CHUNKS_SEQUENTIAL, fa.CHUNKS_PIPELINED
+    # 4096 rows of 896 packs: 448 threads, two packs each (a long streaming call)
+    assert plan(4096, 512, seq) == [("stage1_reduce", 512 * 896 // 256, 256, 1, 8),
+                                    ("stage2_norm", 512, 448, 2, 8)]
+    assert plan(4096, 512, pipe) == [("stage1_reduce", 512 * 896 // 256, 256, 1, 1),
+                                     ("stage_pipe", 1024, 448, 2, 7),
+                                     ("stage2_norm", 512, 448, 2, 1)]
+    # a ragged last chunk: 4096 = 3000 + 1096
+    assert plan(4096, 3000, seq)[1] == ("stage2_norm", 3000, 448, 2, 2)
+    assert plan(4096, 3000, pipe)[1:] == [("stage_pipe", 4096, 448, 2, 1),
+                                          ("stage2_norm", 1096, 448, 2, 1)]
+    # chunks of 2^20 packs and more take the larger flat workgroup
+    assert plan(8192, 1024, seq, n=8, hidden=8192)[0] == ("stage1_reduce", 2048, 512, 1, 8)
+    # one chunk (rows >= m, or -1) is the plain two-stage plan; path 1 ignores the options
+    whole = plan(4096, 0, 0)
+    assert plan(4096, 4096, pipe) == whole and plan(4096, -1, seq) == whole
+    assert [k[0] for k in whole] == ["stage1_reduce", "stage2_norm"]
+    assert plan(4096, 512, pipe, path=1) == plan(4096, 0, 0, path=1)
 
 
 def test_unfused_plan_and_checks():

@@ -111,10 +111,13 @@ def expected_rows(packs, m, forced, capped):
        path=st.integers(min_value=0, max_value=3),
        wave=st.integers(min_value=0, max_value=1), stage1=st.integers(min_value=0, max_value=1),
        block=st.sampled_from([0, 64, 256, 512, 1024]), ppt=st.sampled_from([0, 1, 2, 4]),
-       policy=st.integers(min_value=0, max_value=2))
+       policy=st.integers(min_value=0, max_value=2),
+       rows=st.one_of(st.sampled_from([0, -1, 1, 2, 7, 512, 1024, 1 << 20]),
+                      st.integers(min_value=1, max_value=5000)),
+       sched=st.integers(min_value=0, max_value=2))
 def test_launch_plans_follow_the_geometry_rules(n, m, packs, path, wave, stage1, block, ppt,
-                                                policy):
-    check_plan(n, m, packs, path, wave, stage1, block, ppt, policy)
+                                                policy, rows, sched):
+    check_plan(n, m, packs, path, wave, stage1, block, ppt, policy, rows, sched)
 
 
 def test_launch_plans_on_the_rule_boundaries():
@@ -126,15 +129,31 @@ def test_launch_plans_on_the_rule_boundaries():
             (1, 360, 511, 512, 513, 896, 1024, 1025, 2048, 4096), (0, 1, 2, 3), (0, 1),
             (0, 256), (0, 1, 2, 4), (0, 1, 2)):
         check_plan(n, m, packs, path, 0, stage1, block, ppt, policy)
+    for n, m, packs, rows, sched, stage1, policy in itertools.product(
+            (1, 8), (1, 2, 1024, 1025, 4096, 9000), (1, 896, 2048), (0, -1, 1, 2, 1023, 1024, 4096),
+            (0, 1, 2), (0, 1), (0, 2)):
+        check_plan(n, m, packs, 2, 0, stage1, 0, 0, policy, rows, sched)
 
 
-def check_plan(n, m, packs, path, wave, stage1, block, ppt, policy):
+def expected_flat(n, packs_total, block, stage1):
+    """Workgroup and first-launch grid of a flat kernel over packs_total packs."""
+    if stage1:
+        want_block = 64 * n
+    elif block:
+        want_block = block
+    else:
+        want_block = 512 if packs_total >= (1 << 20) else 256
+    first = min(packs_total, FLAT_PACKS_PER_LAUNCH)
+    return want_block, -(-first // want_block)
+
+
+def check_plan(n, m, packs, path, wave, stage1, block, ppt, policy, rows=0, sched=0):
     hidden = 8 * packs
-    opt = fa.Options(wave, stage1, block, ppt, policy)
+    opt = fa.Options(wave, stage1, block, ppt, policy, rows, sched)
     stream = expected_streaming(n, m, hidden, policy)
     capped = stream and m > 1024
-    rows = expected_rows(packs, m, ppt, capped)
-    if m > 0 and rows is None:
+    rows_geometry = expected_rows(packs, m, ppt, capped)
+    if m > 0 and rows_geometry is None:
         with pytest.raises(fa.FusedArError) as e:
             fa.describe_launch(n, m, hidden, path, opt)
         assert e.value.status == fa.ERR_SHAPE
@@ -146,13 +165,19 @@ def check_plan(n, m, packs, path, wave, stage1, block, ppt, policy):
         assert plan["kernels"] == []
         return
     ks = plan["kernels"]
+    s1 = "stage1_reduce_lds" if stage1 else "stage1_reduce"
+    chunk = m if rows in (0, -1) else min(rows, m)  # two-stage rows per chunk (auto: one chunk)
+    if want_path == 2 and chunk < m:
+        check_chunked_plan(ks, n, m, packs, stage1, block, rows=chunk, pipelined=sched == 2,
+                           geometry=rows_geometry, stream=stream, capped=capped, s1=s1)
+        return
     assert [k["name"] for k in ks] == {
         1: ["onestage"],
-        2: ["stage1_reduce_lds" if stage1 else "stage1_reduce", "stage2_norm"],
-        3: ["stage1_reduce_lds" if stage1 else "stage1_reduce", "residual_add", "rmsnorm"]}[want_path]
+        2: [s1, "stage2_norm"],
+        3: [s1, "residual_add", "rmsnorm"]}[want_path]
     # the row kernel: one workgroup per row, whole waves, every pack of a row covered once
     k_rows = ks[-1]
-    assert (k_rows["per_thread"], k_rows["block"]) == rows
+    assert (k_rows["per_thread"], k_rows["block"]) == rows_geometry
     assert k_rows["grid"] == min(m, ROWS_PER_LAUNCH)
     assert k_rows["launches"] == -(-m // ROWS_PER_LAUNCH)
     assert k_rows["lds_bytes"] == (64 * 1024 if capped else 0)
@@ -160,14 +185,40 @@ def check_plan(n, m, packs, path, wave, stage1, block, ppt, policy):
     # the flat kernels: one pack per thread over all m * packs packs
     total = m * packs
     for k in ks[:-1]:
-        if k["name"] == "stage1_reduce_lds":
-            want_block = 64 * n
-        elif block:
-            want_block = block
-        else:
-            want_block = 512 if total >= (1 << 20) else 256
+        want_block, want_grid = expected_flat(n, total, block, k["name"] == "stage1_reduce_lds")
         assert k["block"] == want_block and k["per_thread"] == 1
-        first = min(total, FLAT_PACKS_PER_LAUNCH)
-        assert k["grid"] == -(-first // want_block)
+        assert k["grid"] == want_grid
         assert k["launches"] == -(-total // FLAT_PACKS_PER_LAUNCH)
         assert k["lds_bytes"] == 0 and k["streaming"] == int(stream)
+
+
+def check_chunked_plan(ks, n, m, packs, stage1, block, rows, pipelined, geometry, stream, capped,
+                       s1):
+    """The two-stage path in chunks of `rows` rows (fewer than m): sequential, a flat reduce and a
+    row launch per chunk; pipelined, the first chunk's reduce, one launch per chunk boundary
+    holding the next chunk's reduce and this chunk's normalisation, and the last chunk's
+    normalisation."""
+    chunks = -(-m // rows)
+    last = m - (chunks - 1) * rows
+    flat_launches = lambda p: -(-p // FLAT_PACKS_PER_LAUNCH)  # noqa: E731
+    names = [s1, "stage_pipe", "stage2_norm"] if pipelined else [s1, "stage2_norm"]
+    assert [k["name"] for k in ks] == names
+    want_block, want_grid = expected_flat(n, rows * packs, block, stage1)
+    f = ks[0]
+    assert (f["block"], f["grid"], f["per_thread"], f["lds_bytes"]) == (want_block, want_grid, 1, 0)
+    assert f["streaming"] == int(stream)
+    if pipelined:
+        assert f["launches"] == flat_launches(rows * packs)
+    else:
+        assert f["launches"] == (chunks - 1) * flat_launches(rows * packs) + flat_launches(last * packs)
+    for k in ks[1:]:
+        assert (k["per_thread"], k["block"]) == geometry
+        assert k["lds_bytes"] == (64 * 1024 if capped else 0) and k["streaming"] == int(stream)
+    norm = ks[-1]
+    if pipelined:
+        pipe = ks[1]
+        assert pipe["grid"] == rows + (last if chunks == 2 else rows)
+        assert pipe["launches"] == chunks - 1
+        assert (norm["grid"], norm["launches"]) == (last, 1)
+    else:
+        assert (norm["grid"], norm["launches"]) == (rows, chunks)
