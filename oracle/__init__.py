@@ -74,13 +74,42 @@ class Oracle:
         m, hidden = residual.shape
         if any(a.shape != (m, hidden) for a in ins) or weight.shape != (hidden,):
             raise ValueError("shape mismatch")
-        arr = (_U16P * len(ins))(*[_ptr(a) for a in ins])
         ro = np.empty((m, hidden), dtype=np.uint16)
         out = np.empty((m, hidden), dtype=np.uint16)
+        self._fused_into(ins, residual, weight, eps, ro, out)
+        return ro, out
+
+    def _fused_into(self, ins, residual, weight, eps, ro, out):
+        m, hidden = residual.shape
+        arr = (_U16P * len(ins))(*[_ptr(a) for a in ins])
         rc = self._lib.oracle_fused_ar_rmsnorm(arr, len(ins), _ptr(residual), _ptr(weight),
                                                float(eps), m, hidden, _ptr(ro), _ptr(out))
         if rc != 0:
             raise ValueError("oracle_fused_ar_rmsnorm rejected its arguments")
+
+    def fused_threads(self, inputs, residual, weight, eps, threads):
+        """``fused`` with the rows cut into ``threads`` contiguous slices, each slice computed by the
+        same single-threaded C function on its own host thread (ctypes releases the GIL during the
+        call). Rows are independent in the oracle, so the result is the same bits as ``fused``."""
+        import concurrent.futures as cf
+        ins = [_as_bits(a) for a in inputs]
+        residual = _as_bits(residual)
+        weight = _as_bits(weight)
+        m, hidden = residual.shape
+        if any(a.shape != (m, hidden) for a in ins) or weight.shape != (hidden,):
+            raise ValueError("shape mismatch")
+        ro = np.empty((m, hidden), dtype=np.uint16)
+        out = np.empty((m, hidden), dtype=np.uint16)
+        threads = max(1, min(int(threads), m))
+        bounds = [(m * t // threads, m * (t + 1) // threads) for t in range(threads)]
+        bounds = [(a, b) for a, b in bounds if b > a]
+
+        def piece(ab):
+            a, b = ab
+            self._fused_into([x[a:b] for x in ins], residual[a:b], weight, eps, ro[a:b], out[a:b])
+
+        with cf.ThreadPoolExecutor(max(1, len(bounds))) as pool:
+            list(pool.map(piece, bounds))
         return ro, out
 
 
@@ -105,3 +134,7 @@ def reduce(inputs):
 
 def fused(inputs, residual, weight, eps):
     return default().fused(inputs, residual, weight, eps)
+
+
+def fused_threads(inputs, residual, weight, eps, threads):
+    return default().fused_threads(inputs, residual, weight, eps, threads)

@@ -1,11 +1,12 @@
 """Parity of the HIP path with the CPU oracle, element by element, through the C ABI.
 
 Bar: `residual_out` and the reduce bit-exact; `out` within 1 bf16 ulp (the kernel's fp32 row
-statistic versus the oracle's binary64 one); no NaN. Problems the oracle finishes in seconds are
-compared whole; the full-size workloads are compared on sampled rows (rows are independent, so
-the oracle computes exactly those rows), always including the first and last row and every
-special row of the stress workload.
+statistic versus the oracle's binary64 one); no NaN. Every problem is compared whole: the
+full-size workloads run the unchanged single-threaded oracle on row slices across the host's
+threads (rows are independent, so the slices together are the oracle's result).
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -51,18 +52,25 @@ def run_gpu(p, path, in_place=False):
     return host(ro), host(out)
 
 
-def sample_rows(p, count=48, seed=0):
-    rng = np.random.default_rng(seed)
-    rows = {0, p.m - 1}
-    rows |= set(rng.choice(p.m, size=min(count, p.m), replace=False).tolist())
-    rows |= set(p.meta.get("zero_rows", [])) | set(p.meta.get("big_rows", []))
-    return np.array(sorted(rows))
+def host_threads():
+    """Host threads for the oracle: those this process may run on, at most 16 (one GPU's share of
+    a shared host)."""
+    try:
+        have = len(os.sched_getaffinity(0))
+    except AttributeError:
+        have = os.cpu_count() or 1
+    return max(1, min(16, have))
 
 
-def oracle_rows(p, rows=None):
-    if rows is None:
-        return oracle.fused(p.inputs, p.residual, p.weight, p.eps)
-    return oracle.fused([x[rows] for x in p.inputs], p.residual[rows], p.weight, p.eps)
+# problems above this many elements run the oracle on row slices across host threads
+THREADED_ORACLE_ELEMENTS = 1 << 22
+
+
+def oracle_rows(p):
+    """The oracle's (residual_out, out) for the whole problem."""
+    if p.n * p.m * p.hidden > THREADED_ORACLE_ELEMENTS:
+        return oracle.fused_threads(p.inputs, p.residual, p.weight, p.eps, host_threads())
+    return oracle.fused(p.inputs, p.residual, p.weight, p.eps)
 
 
 def assert_parity(name, got_ro, got_out, want_ro, want_out):
@@ -76,17 +84,12 @@ def assert_parity(name, got_ro, got_out, want_ro, want_out):
         f"{name}: out differs by {d.max()} ulp at {tuple(np.argwhere(d == d.max())[0])}")
 
 
-def check_problem(p, path, sampled=False):
+def check_problem(p, path):
     name = f"{p.name} n={p.n} m={p.m} hidden={p.hidden} path={path}"
     announce(name)
     ro, out = run_gpu(p, path)
-    if sampled:
-        rows = sample_rows(p)
-        want_ro, want_out = oracle_rows(p, rows)
-        assert_parity(name, ro[rows], out[rows], want_ro, want_out)
-    else:
-        want_ro, want_out = oracle_rows(p)
-        assert_parity(name, ro, out, want_ro, want_out)
+    want_ro, want_out = oracle_rows(p)
+    assert_parity(name, ro, out, want_ro, want_out)
     return ro, out
 
 
@@ -109,8 +112,7 @@ def test_workload(wname, m, path):
     seed = 1000 + m
     p = synth.make_problem(w["n"], m, w["hidden"], seed=seed, eps=w["eps"], dist=w["dist"],
                            name=wname)
-    sampled = m * w["hidden"] * w["n"] > 8 * 1024 * 7168
-    check_problem(p, path, sampled=sampled)
+    check_problem(p, path)
 
 
 def test_paths_agree_bit_for_bit():
@@ -280,12 +282,11 @@ def test_rows_beyond_the_grid():
     """More rows than one launch takes (2^20 workgroups): the rows come in two launches."""
     m = (1 << 20) + 3
     p = synth.make_problem(2, m, 8, seed=12, name="row stride")
+    want_ro, want_out = oracle_rows(p)
     for path in (1, 2):
         announce(f"row stride path={path}")
         ro, out = run_gpu(p, path)
-        rows = np.array([0, 1, (1 << 20) - 1, 1 << 20, (1 << 20) + 1, m - 1])
-        want_ro, want_out = oracle_rows(p, rows)
-        assert_parity("row stride", ro[rows], out[rows], want_ro, want_out)
+        assert_parity("row stride", ro, out, want_ro, want_out)
 
 
 def test_flat_packs_beyond_one_launch():
@@ -471,12 +472,8 @@ def test_unfused_matches_fused_bit_for_bit(n, m, hidden):
     torch.cuda.synchronize()
     assert torch.equal(ro_u.view(torch.int16), ro_f.view(torch.int16))
     assert torch.equal(out_u.view(torch.int16), out_f.view(torch.int16))
-    rows = sample_rows(p, count=16) if m > 64 else None
-    want_ro, want_out = oracle_rows(p, rows)
-    got_ro, got_out = host(ro_u), host(out_u)
-    if rows is not None:
-        got_ro, got_out = got_ro[rows], got_out[rows]
-    assert_parity("unfused", got_ro, got_out, want_ro, want_out)
+    want_ro, want_out = oracle_rows(p)
+    assert_parity("unfused", host(ro_u), host(out_u), want_ro, want_out)
 
 
 def test_unfused_in_place_residual():
@@ -500,14 +497,25 @@ OPTION_SETS = [
     (fa.WAVE_DPP, fa.STAGE1_FLAT, 64, 0, fa.LOAD_STREAM),
     (fa.WAVE_DPP, fa.STAGE1_FLAT, 1024, 0, 0),
     (fa.WAVE_DPP, fa.STAGE1_FLAT, 0, 0, fa.LOAD_STREAM),
+    # the two-stage path in chunks of 7 rows (ragged last chunk), sequential and pipelined
+    (fa.WAVE_DPP, fa.STAGE1_FLAT, 0, 0, 0, 7, fa.CHUNKS_SEQUENTIAL),
+    (fa.WAVE_DPP, fa.STAGE1_FLAT, 0, 0, 0, 7, fa.CHUNKS_PIPELINED),
+    (fa.WAVE_BPERMUTE, fa.STAGE1_LDS, 0, 0, fa.LOAD_STREAM, 2, fa.CHUNKS_SEQUENTIAL),
+    (fa.WAVE_DPP, fa.STAGE1_FLAT, 256, 0, fa.LOAD_STREAM, 1, fa.CHUNKS_PIPELINED),
 ]
 
 
-@pytest.mark.parametrize("opt", OPTION_SETS, ids=lambda o: "w{}-s{}-b{}-p{}-l{}".format(*o))
+def _option_id(o):
+    o = tuple(o) + (0,) * (7 - len(o))
+    return "w{}-s{}-b{}-p{}-l{}-r{}-c{}".format(*o)
+
+
+@pytest.mark.parametrize("opt", OPTION_SETS, ids=_option_id)
 @pytest.mark.parametrize("n,m,hidden", [(8, 37, 7168), (3, 11, 520), (5, 300, 2880), (1, 9, 64)])
 def test_design_options_are_bit_identical(opt, n, m, hidden):
-    """The ds_bpermute wave reduction, the LDS-staged stage 1 and other stage-1 workgroup sizes
-    give exactly the default kernels' bits on both paths (and so the oracle's)."""
+    """The ds_bpermute wave reduction, the LDS-staged stage 1, other stage-1 workgroup sizes and
+    the two-stage path in chunks of rows give exactly the default kernels' bits on every path
+    (and so the oracle's)."""
     p = synth.make_problem(n, m, hidden, seed=19, name="options")
     ins = [dev(x) for x in p.inputs]
     res, w = dev(p.residual), dev(p.weight)
@@ -520,6 +528,24 @@ def test_design_options_are_bit_identical(opt, n, m, hidden):
         assert torch.equal(out_o.view(torch.int16), out_d.view(torch.int16)), path
     want_ro, want_out = oracle_rows(p)
     assert_parity("options", host(ro_o), host(out_o), want_ro, want_out)
+
+
+@pytest.mark.parametrize("schedule", [fa.CHUNKS_SEQUENTIAL, fa.CHUNKS_PIPELINED])
+def test_chunked_two_stage_on_a_long_streaming_call(schedule):
+    """The two-stage path in chunks of 512 rows on a call that streams and caps its row
+    workgroups (two packs per thread): the oracle's result, and path 1's bits."""
+    p = synth.make_problem(4, 2100, 7168, seed=23, name="chunks")
+    ins = [dev(x) for x in p.inputs]
+    res, w = dev(p.residual), dev(p.weight)
+    announce(f"chunked two-stage schedule={schedule} n=4 m=2100 hidden=7168")
+    ro1, out1 = fa.fused_ar_rmsnorm(ins, res, w, p.eps, path=1)
+    ro, out = fa.fused_ar_rmsnorm(ins, res, w, p.eps, path=2,
+                                  options=fa.Options(0, 0, 0, 0, 0, 512, schedule))
+    torch.cuda.synchronize()
+    assert torch.equal(ro.view(torch.int16), ro1.view(torch.int16))
+    assert torch.equal(out.view(torch.int16), out1.view(torch.int16))
+    want_ro, want_out = oracle_rows(p)
+    assert_parity("chunks", host(ro), host(out), want_ro, want_out)
 
 
 @pytest.mark.parametrize("ppt", [1, 2, 4])
@@ -543,8 +569,8 @@ def test_forced_packs_per_thread(ppt):
 
 def test_randomized_shapes_paths_and_options():
     """80 seeded random cases: n in 1..8, m in 1..300, hidden any multiple of 8 up to 9600, every
-    path (auto, one-stage, two-stage, unfused), random design options and eps, normal or stress
-    values; each compared whole with the oracle."""
+    path (auto, one-stage, two-stage, unfused), random design options (chunked two-stage
+    schedules included) and eps, normal or stress values; each compared whole with the oracle."""
     rng = np.random.default_rng(2024)
     for case in range(80):
         n = int(rng.integers(1, 9))
@@ -555,13 +581,14 @@ def test_randomized_shapes_paths_and_options():
         if (hidden // 8 + max(ppt, 1) - 1) // max(ppt, 1) > 1024:
             ppt = 0
         opt = fa.Options(int(rng.integers(0, 2)), int(rng.integers(0, 2)),
-                         int(rng.choice([0, 64, 256, 512, 1024])), ppt, int(rng.integers(0, 3)))
+                         int(rng.choice([0, 64, 256, 512, 1024])), ppt, int(rng.integers(0, 3)),
+                         int(rng.choice([0, 0, 1, 13, 64])), int(rng.integers(0, 3)))
         eps = float(rng.choice([1e-6, 1e-5, 0.1]))
         dist = "stress" if rng.random() < 0.3 else "normal"
         p = synth.make_problem(n, m, hidden, seed=5000 + case, eps=eps, dist=dist, name="random")
         name = (f"random case {case}: n={n} m={m} hidden={hidden} path={path} "
                 f"options=({opt.wave_reduce},{opt.stage1},{opt.stage1_block},{opt.packs_per_thread},"
-                f"{opt.load_policy}) "
+                f"{opt.load_policy},{opt.stage_rows},{opt.schedule}) "
                 f"eps={eps} {dist}")
         announce(name)
         ins = [dev(x) for x in p.inputs]
@@ -671,7 +698,7 @@ def test_split_rows_randomized():
 def test_long_streaming_calls_randomized():
     """8 seeded random calls long enough to stream from HBM (over 128 MiB read, over 1024 rows),
     where the row kernels are capped at two workgroups per CU and take 1, 2 or 4 packs per thread
-    by row width: sampled rows against the oracle, and paths 1 and 2 and the unfused sequence
+    by row width: path 1 whole against the oracle, and paths 1 and 2 and the unfused sequence
     bit-identical to each other."""
     rng = np.random.default_rng(2026)
     for case in range(8):
@@ -694,9 +721,8 @@ def test_long_streaming_calls_randomized():
             got[path] = (ro.view(torch.int16), out.view(torch.int16))
         for path in (2, fa.PATH_UNFUSED):
             assert torch.equal(got[path][0], got[1][0]) and torch.equal(got[path][1], got[1][1]), path
-        rows = sample_rows(p, count=24, seed=case)
-        want_ro, want_out = oracle_rows(p, rows)
-        assert_parity(name, host(got[1][0].view(torch.bfloat16))[rows],
-                      host(got[1][1].view(torch.bfloat16))[rows], want_ro, want_out)
+        want_ro, want_out = oracle_rows(p)
+        assert_parity(name, host(got[1][0].view(torch.bfloat16)),
+                      host(got[1][1].view(torch.bfloat16)), want_ro, want_out)
         del ins, res, got
         torch.cuda.empty_cache()
