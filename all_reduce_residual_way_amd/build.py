@@ -9,9 +9,6 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 SOURCES = [os.path.join(CSRC, "fused_ar.hip")]
 LIBRARY = os.path.join(PKG, "libfused_ar.so")
-# HBM ceiling probes for the benchmark (not part of the fused path)
-PROBE_SOURCES = [os.path.join(CSRC, "hbm_probe.hip")]
-PROBE_LIBRARY = os.path.join(PKG, "libhbm_probe.so")
 ARCH = "gfx950"
 
 FLAGS = [
@@ -42,11 +39,5 @@ def build(output=LIBRARY, extra_flags=(), verbose=False, sources=SOURCES):
     return output
 
 
-def build_probe(verbose=False):
-    """Compile the HBM ceiling probes into libhbm_probe.so; returns its path."""
-    return build(PROBE_LIBRARY, verbose=verbose, sources=PROBE_SOURCES)
-
-
 if __name__ == "__main__":
     print(build(verbose=True))
-    print(build_probe(verbose=True))

@@ -29,6 +29,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_onestage_n8_m4096_h7168.t
 KERNEL_SOURCES = [os.path.join(ROOT, "all_reduce_residual_way_amd", "csrc", f)
                   for f in ("kernels.h", "bf16x8.h", "wave_sum.h", "fused_ar.hip")]
 DECODE_M = (1, 2, 4, 8, 16, 32)
+METRIC_ROWS_M = (2048, 4096, 8192)  # the bandwidth rows of the metric: N = 8, hidden = 7168
 SPLIT = "split"  # Workload.call: the split-row entry point (slices chosen by the library)
 
 
@@ -63,7 +64,14 @@ def parse_args():
                          "inputs, default 8): one JSON line per shape")
     ap.add_argument("--all-workloads", action="store_true",
                     help="only measure every workload of the decode/prefill set on each of its "
-                         "paths: one JSON line per (workload, m, path)")
+                         "paths, with the CPU oracle timed on the same inputs: one JSON line per "
+                         "(workload, m, path), then one per (workload, m) for the oracle")
+    ap.add_argument("--path-sweep", action="store_true",
+                    help="only compare path 1 with path 2 over n in {2, 4, 8}, six row widths and "
+                         "row counts 1..8192: one JSON line per shape (the one-GPU path rule)")
+    ap.add_argument("--chunk-sweep", action="store_true",
+                    help="only time the two-stage path whole and in row chunks (sequential and "
+                         "pipelined) on the HBM-cold shapes: one JSON line per shape")
     return ap.parse_args()
 
 
@@ -125,21 +133,15 @@ def copy_calibration(torch):
 
 
 def hbm_ceilings(torch):
-    """Practical HBM ceilings on this GPU from the plain streaming kernels of libhbm_probe.so: one
+    """Practical HBM ceilings on this GPU from the plain streaming kernels of hbm_probe/ (libhbm_probe.so): one
     read stream, a copy, and the one-stage kernel's mix of nine read and two write streams at its
     bench shape (N=8, m=4096, hidden=7168), each over a few launch shapes and cache policies,
     HBM-cold (4 GiB read buffer; 2 GiB copies; two alternating mix sets of 646 MB); then the
     one-stage kernel itself on that shape in the same process. One JSON line per measurement, then
     a summary line with the best of each and the kernel's rate over the best mix."""
-    import ctypes
-    from all_reduce_residual_way_amd import build as hip_build
-    if not os.path.exists(hip_build.PROBE_LIBRARY):
-        raise RuntimeError(f"{hip_build.PROBE_LIBRARY} is not built")
-    lib = ctypes.CDLL(hip_build.PROBE_LIBRARY)
-    vp, sz, ci = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
-    lib.hbm_probe_read.argtypes = [vp, sz, vp, ci, ci, ci, vp]
-    lib.hbm_probe_copy.argtypes = [vp, vp, sz, ci, ci, vp]
-    lib.hbm_probe_mix.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), sz, ci, ci, vp]
+    import hbm_probe
+    lib = hbm_probe.load()
+    vp = ctypes.c_void_p
     stream = torch.cuda.current_stream().cuda_stream
 
     def timed_ms(fn, reps):
@@ -308,11 +310,15 @@ def parity_rows(m):
 
 def host_threads():
     """Host threads this process may use, at most 16 (one GPU's share of a shared host)."""
+    return max(1, min(16, host_affinity()))
+
+
+def host_affinity():
+    """CPUs this process may run on (its affinity mask; all CPUs where there is no mask)."""
     try:
-        have = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:
-        have = os.cpu_count() or 1
-    return max(1, min(16, have))
+        return os.cpu_count() or 1
 
 
 def host_cpu_model():
@@ -327,39 +333,38 @@ def host_cpu_model():
     return None
 
 
-def oracle_all_cores(oracle, prob, eps, bytes_alg, seconds):
-    """The unchanged oracle on row slices, one slice per host thread (ctypes drops the GIL).
+def host_info():
+    return {"cpu": host_cpu_model(), "host_cpus": os.cpu_count(), "affinity_cpus": host_affinity()}
 
-    Rows are independent, so the slices together give exactly the single-threaded result; the
-    first pass is checked against one single-threaded pass of the same rows.
-    """
-    import concurrent.futures as cf
+
+def oracle_runs(bytes_alg):
+    """Single-threaded oracle runs per timed problem: the median of 5, or one run when a pass
+    moves more than 1 GB (at about 0.35 GB/s that is several seconds already)."""
+    return 1 if bytes_alg > 1e9 else 5
+
+
+def time_oracle(oracle, prob, eps, bytes_alg):
+    """The unchanged oracle on the whole problem: single-threaded (median of oracle_runs passes)
+    and on row slices over host_threads() threads (ctypes drops the GIL; rows are independent, so
+    the slices give the single-threaded result, checked here bit for bit). Returns a dict."""
     import numpy as np
+    runs = oracle_runs(bytes_alg)
+    times = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        ro1, out1 = oracle.fused(prob.inputs, prob.residual, prob.weight, eps)
+        times.append(time.perf_counter() - t0)
+    t1 = float(np.median(times))
     threads = host_threads()
-    m = prob.residual.shape[0]
-    bounds = [(m * t // threads, m * (t + 1) // threads) for t in range(threads)]
-    bounds = [(a, b) for a, b in bounds if b > a]
-
-    def piece(ab):
-        a, b = ab
-        return oracle.fused([x[a:b] for x in prob.inputs], prob.residual[a:b], prob.weight, eps)
-
-    with cf.ThreadPoolExecutor(len(bounds)) as pool:
-        passes, t0 = 0, time.perf_counter()
-        while True:
-            parts = list(pool.map(piece, bounds))
-            passes += 1
-            elapsed = time.perf_counter() - t0
-            if passes == 1:
-                first = parts
-            if elapsed >= seconds:
-                break
-    a, b = bounds[0]
-    ro1, out1 = oracle.fused([x[a:b] for x in prob.inputs], prob.residual[a:b], prob.weight, eps)
-    same = bool(np.array_equal(first[0][0], ro1) and np.array_equal(first[0][1], out1))
-    return {"value": round(passes * bytes_alg / elapsed / 1e9, 4), "unit": "GB/s",
-            "cores": len(bounds), "passes": passes, "seconds": round(elapsed, 2),
-            "first_slice_matches_single_thread": same}
+    t0 = time.perf_counter()
+    ro_t, out_t = oracle.fused_threads(prob.inputs, prob.residual, prob.weight, eps, threads)
+    tt = time.perf_counter() - t0
+    same = bool(np.array_equal(ro1, ro_t) and np.array_equal(out1, out_t))
+    return {"oracle_1t_ms": round(t1 * 1e3, 3), "oracle_1t_runs": runs,
+            "oracle_1t_gbs": round(bytes_alg / t1 / 1e9, 4),
+            "oracle_threads": threads, "oracle_threads_ms": round(tt * 1e3, 3),
+            "oracle_threads_gbs": round(bytes_alg / tt / 1e9, 4),
+            "threads_match_single": same}
 
 
 def per_rank_share(torch, fa, work, steps, warmup):
@@ -402,11 +407,33 @@ def per_rank_share(torch, fa, work, steps, warmup):
             "twostage_share_us": round(t1 + t2, 3)}
 
 
-def all_workloads(torch, fa, synth):
-    """Each workload on its own path(s) and on paths 1 and 2. Problems whose buffers fit in the
-    256 MB Infinity Cache are timed as the pages time decode: one warm buffer set, calls captured in
-    one HIP graph (2000, fewer for long calls), min over 20 replays, per call. Larger ones run
-    back-to-back calls rotating enough buffer sets to exceed 1 GiB, so that HBM serves them."""
+def timing_for(work, path, footprint, bytes_alg, options=None):
+    """Per-call microseconds of one problem and how they were taken. Problems whose buffers fit in
+    the 256 MB Infinity Cache (footprint <= 128 MiB) are timed as the pages time decode: one warm
+    buffer set, calls captured in one HIP graph (2000, fewer for long calls), min over 20 replays,
+    per call. Larger ones run 100 back-to-back calls over the workload's buffer sets."""
+    if footprint <= (128 << 20):
+        est_us = 4.0 + bytes_alg / 5e3  # rough per-call time, to size the graph
+        calls = int(max(50, min(2000, 40e3 / est_us)))
+        return (work.graph_latency_us(path, options, calls=calls, replays=20),
+                f"warm, graph of {calls} calls, min of 20 replays")
+    copies = len(work.sets)
+    return (work.time_ms(path, 100, 10, options) * 1e3,
+            f"100 calls over {copies} buffer sets ({copies * footprint >> 20} MiB)")
+
+
+def cold_copies(footprint):
+    """Buffer sets that make a timed loop read beyond the Infinity Cache (>= 1 GiB in total);
+    one for problems that fit the cache (they are timed warm)."""
+    if footprint <= (128 << 20):
+        return 1
+    return min(8, max(1, -(-(1 << 30) // footprint)))
+
+
+def all_workloads(torch, fa, synth, oracle):
+    """Each workload on its own path(s) and on paths 1 and 2 (timing_for), then the CPU oracle on
+    the same inputs (time_oracle): single-threaded and over host threads."""
+    print(json.dumps({"host": host_info(), "oracle_threads": host_threads()}), flush=True)
     for wname, w in synth.WORKLOADS.items():
         ms = w["ms"] if w["ms"] is not None else synth.stress_m_values(0)
         paths = sorted(set(w["paths"]) | {1, 2})
@@ -415,20 +442,10 @@ def all_workloads(torch, fa, synth):
             prob = synth.make_problem(n, m, hidden, seed=1000 + m, eps=w["eps"], dist=w["dist"],
                                       name=wname)
             footprint = 2 * (n + 3) * m * hidden
-            warm = footprint <= (128 << 20)
-            copies = 1 if warm else min(8, max(1, -(-(1 << 30) // footprint)))
-            work = Workload(torch, fa, prob, copies)
+            work = Workload(torch, fa, prob, cold_copies(footprint))
             bytes_alg = algorithmic_bytes(n, m, hidden)
             for p in paths:
-                if warm:
-                    est_us = 4.0 + bytes_alg / 5e3  # rough per-call time, to size the graph
-                    calls = int(max(50, min(2000, 40e3 / est_us)))
-                    us = work.graph_latency_us(p, calls=calls, replays=20)
-                    how = f"warm, graph of {calls} calls, min of 20 replays"
-                else:
-                    steps = 100
-                    us = work.time_ms(p, steps, 10) * 1e3
-                    how = f"{steps} calls over {copies} buffer sets ({copies * footprint >> 20} MiB)"
+                us, how = timing_for(work, p, footprint, bytes_alg)
                 gbs = bytes_alg / (us * 1e-6) / 1e9
                 print(json.dumps({"workload": wname, "n": n, "m": m, "hidden": hidden,
                                   "eps": w["eps"], "dist": w["dist"], "path": p,
@@ -437,6 +454,68 @@ def all_workloads(torch, fa, synth):
                                   "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
                                   "timing": how}), flush=True)
             del work
+            torch.cuda.empty_cache()
+            print(json.dumps({"workload": wname, "n": n, "m": m, "hidden": hidden,
+                              **time_oracle(oracle, prob, w["eps"], bytes_alg)}), flush=True)
+
+
+PATH_SWEEP_N = (2, 4, 8)
+PATH_SWEEP_HIDDEN = (2880, 4096, 7168, 8192, 16384, 32768)
+PATH_SWEEP_M = (1, 2, 8, 16, 17, 32, 33, 64, 256, 1024, 2048, 4096, 8192)
+
+
+def path_sweep(torch, fa):
+    """Path 1 against path 2 on one GPU over n x row width x row count (timing_for; the buffers
+    are filled on the GPU). One JSON line per shape; shapes whose buffers exceed 3 GiB are
+    skipped."""
+    for n in PATH_SWEEP_N:
+        for hidden in PATH_SWEEP_HIDDEN:
+            for m in PATH_SWEEP_M:
+                footprint = 2 * (n + 3) * m * hidden
+                if footprint > (3 << 30):
+                    continue
+                work = DeviceWorkload(torch, fa, n, m, hidden, cold_copies(footprint),
+                                      seed=n + hidden + m)
+                bytes_alg = algorithmic_bytes(n, m, hidden)
+                us = {}
+                for p in (1, 2):
+                    us[p], how = timing_for(work, p, footprint, bytes_alg)
+                print(json.dumps({"n": n, "m": m, "hidden": hidden,
+                                  "path1_us": round(us[1], 3), "path2_us": round(us[2], 3),
+                                  "path2_over_path1": round(us[2] / us[1], 3),
+                                  "auto_path": fa.auto_path(n, m, hidden), "timing": how}),
+                      flush=True)
+                del work
+                torch.cuda.empty_cache()
+
+
+CHUNK_SWEEP_SHAPES = ((4, 4096, 7168), (8, 8192, 8192), (8, 2048, 7168), (8, 4096, 7168),
+                      (8, 8192, 7168))
+CHUNK_SWEEP_ROWS = (256, 512, 1024, 2048)
+
+
+def chunk_sweep(torch, fa):
+    """The two-stage path whole and in chunks of rows, sequential and pipelined, against path 1,
+    on HBM-cold shapes (buffer sets of >= 1 GiB): 60 calls per variant, best of three rounds."""
+    for n, m, hidden in CHUNK_SWEEP_SHAPES:
+        footprint = 2 * (n + 3) * m * hidden
+        work = DeviceWorkload(torch, fa, n, m, hidden, cold_copies(footprint), seed=m + hidden)
+        bytes_alg = algorithmic_bytes(n, m, hidden)
+        variants = [("path1", 1, None), ("path2", 2, None)]
+        for r in CHUNK_SWEEP_ROWS:
+            if r < m:
+                variants += [(f"sequential_{r}", 2, fa.Options(0, 0, 0, 0, 0, r, fa.CHUNKS_SEQUENTIAL)),
+                             (f"pipelined_{r}", 2, fa.Options(0, 0, 0, 0, 0, r, fa.CHUNKS_PIPELINED))]
+        best = {}
+        for _ in range(3):
+            for name, p, o in variants:
+                best[name] = min(best.get(name, 1e30), work.time_ms(p, 60, 6, o) * 1e3)
+        print(json.dumps({"n": n, "m": m, "hidden": hidden, "buffer_sets": len(work.sets),
+                          "us_per_call": {k: round(v, 2) for k, v in best.items()},
+                          "pct_of_hbm_peak": {k: round(100 * bytes_alg / (v * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)
+                                              for k, v in best.items()}}), flush=True)
+        del work
+        torch.cuda.empty_cache()
 
 
 class DeviceWorkload(Workload):
@@ -469,25 +548,15 @@ SWEEP_M = (1, 32, 256, 1024, 4096, 16384)
 
 def sweep(torch, fa, n=8):
     """Path 1 over a grid of row widths and row counts (n inputs, from --n): one JSON line per
-    shape. Timing as in all_workloads (warm graphs up to 128 MiB of buffers, HBM-cold rotation
-    above); shapes whose buffers exceed 2 GiB are skipped."""
+    shape, timed by timing_for; shapes whose buffers exceed 2 GiB are skipped."""
     for hidden in SWEEP_HIDDEN:
         for m in SWEEP_M:
             footprint = 2 * (n + 3) * m * hidden
             if footprint > (2 << 30):
                 continue
-            warm = footprint <= (128 << 20)
-            copies = 1 if warm else min(8, max(1, -(-(1 << 30) // footprint)))
-            work = DeviceWorkload(torch, fa, n, m, hidden, copies, seed=hidden + m)
+            work = DeviceWorkload(torch, fa, n, m, hidden, cold_copies(footprint), seed=hidden + m)
             bytes_alg = algorithmic_bytes(n, m, hidden)
-            if warm:
-                est_us = 4.0 + bytes_alg / 5e3
-                calls = int(max(50, min(2000, 40e3 / est_us)))
-                us = work.graph_latency_us(1, calls=calls, replays=20)
-                how = f"warm, graph of {calls} calls, min of 20 replays"
-            else:
-                us = work.time_ms(1, 60, 10) * 1e3
-                how = f"60 calls over {copies} buffer sets ({copies * footprint >> 20} MiB)"
+            us, how = timing_for(work, 1, footprint, bytes_alg)
             k = fa.describe_launch(n, m, hidden, 1)["kernels"][0]
             gbs = bytes_alg / (us * 1e-6) / 1e9
             print(json.dumps({"n": n, "m": m, "hidden": hidden, "us_per_call": round(us, 3),
@@ -524,7 +593,14 @@ def main():
         copy_calibration(torch)
         return
     if args.all_workloads:
-        all_workloads(torch, fa, synth)
+        import oracle  # the CPU baseline beside each row
+        all_workloads(torch, fa, synth, oracle)
+        return
+    if args.path_sweep:
+        path_sweep(torch, fa)
+        return
+    if args.chunk_sweep:
+        chunk_sweep(torch, fa)
         return
     if args.ceilings:
         hbm_ceilings(torch)
@@ -573,6 +649,24 @@ def main():
                         "gbs_algorithmic": round(bytes_alg / (sms * 1e-3) / 1e9, 1),
                         "kernels": ["split_reduce", "split_norm"],
                         "slices": work.ws_bytes // (4 * m)}
+
+    # the other rows the metric is quoted on (N = 8, hidden = 7168, m >= 2048), path 1, HBM-cold
+    metric_rows = {}
+    for mm in METRIC_ROWS_M:
+        if mm == m and (n, hidden, path) == (8, 7168, 1):
+            metric_rows[str(mm)] = {"us_per_call": round(ms * 1e3, 3), "gbs_algorithmic": round(gbs, 1),
+                                    "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+            continue
+        log(f"metric row m={mm}")
+        fp = 2 * (8 + 3) * mm * 7168
+        mw = DeviceWorkload(torch, fa, 8, mm, 7168, min(8, max(1, -(-(1 << 30) // fp))), seed=mm)
+        mus = mw.time_ms(1, max(short, 20), args.warmup) * 1e3
+        mg = algorithmic_bytes(8, mm, 7168) / (mus * 1e-6) / 1e9
+        metric_rows[str(mm)] = {"us_per_call": round(mus, 3), "gbs_algorithmic": round(mg, 1),
+                                "pct_of_hbm_peak": round(100 * mg / HBM_PEAK_GBS, 2),
+                                "buffer_sets": len(mw.sets)}
+        del mw
+        torch.cuda.empty_cache()
 
     extra = None
     if not args.no_extra:
@@ -653,11 +747,17 @@ def main():
             if elapsed >= args.cpu_seconds:
                 break
         cpu = {"value": round(passes * bytes_alg / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1,
-               "kind": "oracle", "cpu": host_cpu_model(),
+               "kind": "oracle",
                "sample": f"the whole timed workload (n={n}, m={m}, hidden={hidden}), {passes} "
-                         f"pass(es) in {elapsed:.1f} s, single-threaded C oracle"}
+                         f"pass(es) in {elapsed:.1f} s, single-threaded C oracle",
+               **host_info()}
         if not args.no_extra:
-            extra["cpu_oracle_all_cores"] = oracle_all_cores(oracle, prob, eps, bytes_alg, args.cpu_seconds / 2)
+            log("timing the CPU oracle on host threads")
+            t = time_oracle(oracle, prob, eps, bytes_alg)
+            extra["cpu_oracle_threads"] = {
+                "value": t["oracle_threads_gbs"], "unit": "GB/s", "cores": t["oracle_threads"],
+                "matches_single_thread": t["threads_match_single"],
+                "sample": "the whole timed workload, rows cut into one slice per thread, one pass"}
 
     traffic = measured_traffic() if (n, m, hidden, path) == (8, 4096, 7168, 1) else None
     props = torch.cuda.get_device_properties(0)
@@ -687,6 +787,7 @@ def main():
                      "algorithmic_bytes_per_launch": bytes_alg},
         "cpu_baseline": cpu,
         "paths": paths,
+        "metric_rows_n8_h7168_path1": metric_rows,
         "decode_us_per_call": decode,
         "decode_designs_us_per_call": decode_designs,
         "split_rows_us_per_call": split_rows,

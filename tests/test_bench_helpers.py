@@ -52,19 +52,25 @@ def test_digest_ignores_comments_but_not_code(tmp_path, monkeypatch):
     assert bench.kernel_source_digest() != base
 
 
-def test_oracle_all_cores_matches_single_thread():
-    import numpy as np
+def test_oracle_timing_on_threads_matches_single_thread():
     import oracle
     from all_reduce_residual_way_amd import synth
     prob = synth.make_problem(4, 37, 64, seed=5)
-    got = bench.oracle_all_cores(oracle.default(), prob, prob.eps, 1000, 0.0)
-    assert got["first_slice_matches_single_thread"] and got["passes"] == 1
-    assert 1 <= got["cores"] <= 16
-    # the slices cover every row exactly once: reassemble and compare with one whole pass
-    m, threads = 37, got["cores"]
-    bounds = [(m * t // threads, m * (t + 1) // threads) for t in range(threads)]
-    parts = [oracle.fused([x[a:b] for x in prob.inputs], prob.residual[a:b], prob.weight, prob.eps)
-             for a, b in bounds if b > a]
-    whole = oracle.fused(prob.inputs, prob.residual, prob.weight, prob.eps)
-    assert np.array_equal(np.concatenate([p[0] for p in parts]), whole[0])
-    assert np.array_equal(np.concatenate([p[1] for p in parts]), whole[1])
+    got = bench.time_oracle(oracle.default(), prob, prob.eps, 10_000)
+    assert got["threads_match_single"]
+    assert got["oracle_1t_runs"] == 5 and 1 <= got["oracle_threads"] <= 16
+    assert got["oracle_1t_ms"] > 0 and got["oracle_threads_ms"] > 0
+    assert bench.oracle_runs(2e9) == 1 and bench.oracle_runs(5e8) == 5
+
+
+def test_host_info_names_cpus():
+    info = bench.host_info()
+    assert info["host_cpus"] >= 1 and 1 <= info["affinity_cpus"] <= info["host_cpus"]
+    assert bench.host_threads() == min(16, info["affinity_cpus"])
+
+
+def test_cold_copies_exceed_the_cache():
+    assert bench.cold_copies(100 << 20) == 1          # timed warm
+    for fp in (200 << 20, 646 << 20, 1 << 30, 3 << 30):
+        c = bench.cold_copies(fp)
+        assert c * fp >= (1 << 30) or c == 8

@@ -7,21 +7,17 @@ import os
 import pytest
 import torch  # before the probe library, so that it binds to torch's HIP runtime
 
-from all_reduce_residual_way_amd import build as hip_build
+import hbm_probe
 
-VP, SZ, CI = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+VP = ctypes.c_void_p
 FAKE = 0x7F0000000000  # aligned, never dereferenced: every call below is rejected before a launch
 
 
 @pytest.fixture(scope="module")
 def probe():
-    if not os.path.exists(hip_build.PROBE_LIBRARY):
-        pytest.fail(f"{hip_build.PROBE_LIBRARY} is not built")
-    lib = ctypes.CDLL(hip_build.PROBE_LIBRARY)
-    lib.hbm_probe_read.argtypes = [VP, SZ, VP, CI, CI, CI, VP]
-    lib.hbm_probe_copy.argtypes = [VP, VP, SZ, CI, CI, VP]
-    lib.hbm_probe_mix.argtypes = [ctypes.POINTER(VP), ctypes.POINTER(VP), SZ, CI, CI, VP]
-    return lib
+    if not os.path.exists(hbm_probe.LIBRARY):
+        pytest.fail(f"{hbm_probe.LIBRARY} is not built")
+    return hbm_probe.load()
 
 
 def test_probe_arguments_rejected_before_launch(probe):
