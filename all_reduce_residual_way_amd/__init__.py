@@ -17,7 +17,7 @@ __all__ = [
     "fused_ar_reduce", "fused_ar_rmsnorm_split", "split_workspace_bytes",
     "fused_ar_rmsnorm_split_ptrs", "fused_ar_rmsnorm_ptrs", "fused_ar_rmsnorm_ex_ptrs",
     "fused_ar_unfused_rmsnorm_ptrs", "fused_ar_reduce_ptrs", "fused_ar_rmsnorm_check_ptrs",
-    "auto_path", "describe_launch", "strerror",
+    "auto_path", "auto_path_tp", "describe_launch", "strerror",
     "OK", "ERR_INVALID", "ERR_SHAPE", "ERR_ALIGN", "ERR_ALIAS",
     "PATH_AUTO", "PATH_ONESTAGE", "PATH_TWOSTAGE", "PATH_UNFUSED", "WAVE_DPP", "WAVE_BPERMUTE",
     "STAGE1_FLAT", "STAGE1_LDS", "LOAD_AUTO", "LOAD_CACHED", "LOAD_STREAM", "CHUNKS_AUTO",
@@ -108,6 +108,8 @@ def library():
         lib.fused_ar_reduce.restype = ctypes.c_int
         lib.fused_ar_auto_path.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
         lib.fused_ar_auto_path.restype = ctypes.c_int
+        lib.fused_ar_auto_path_tp.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        lib.fused_ar_auto_path_tp.restype = ctypes.c_int
         lib.fused_ar_describe_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                  ctypes.c_int, ctypes.POINTER(_LaunchPlan)]
         lib.fused_ar_describe_launch.restype = ctypes.c_int
@@ -128,8 +130,14 @@ def strerror(status):
 
 
 def auto_path(n, m, hidden):
-    """The path (1 or 2) that ``path=0`` selects; negative status for bad arguments."""
+    """The path (1 or 2) that ``path=0`` selects on one GPU; negative status for bad arguments."""
     return library().fused_ar_auto_path(int(n), int(m), int(hidden))
+
+
+def auto_path_tp(n, m, hidden):
+    """The pages' path rule for a tensor-parallel group over n GPUs (1 or 2); negative status for
+    bad arguments."""
+    return library().fused_ar_auto_path_tp(int(n), int(m), int(hidden))
 
 
 def describe_launch(n, m, hidden, path=PATH_AUTO, options=None):
@@ -271,7 +279,16 @@ def _stream_handle(stream, device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _prepare(inputs, residual, weight, residual_out, out):
+def _on_stream(t, stream):
+    """A tensor allocated here for work enqueued on ``stream`` (not the current stream): recorded
+    on that stream, so that torch's caching allocator does not hand its memory out again before
+    that work is done, even if the caller drops the tensor at once."""
+    if stream is not None:
+        t.record_stream(stream)
+    return t
+
+
+def _prepare(inputs, residual, weight, residual_out, out, stream=None):
     torch = _torch_module()
     if not isinstance(inputs, (list, tuple)) or not inputs:
         raise ValueError("inputs must be a non-empty list of tensors")
@@ -288,11 +305,11 @@ def _prepare(inputs, residual, weight, residual_out, out):
         _check_tensor(residual, "residual", (m, hidden), device)
         _check_tensor(weight, "weight", (hidden,), device)
     if residual_out is None:
-        residual_out = torch.empty_like(residual)
+        residual_out = _on_stream(torch.empty_like(residual), stream)
     elif not _fits(residual_out, shape, index, torch):
         _check_tensor(residual_out, "residual_out", (m, hidden), device)
     if out is None:
-        out = torch.empty_like(residual)
+        out = _on_stream(torch.empty_like(residual), stream)
     elif not _fits(out, shape, index, torch):
         _check_tensor(out, "out", (m, hidden), device)
     return m, hidden, device, residual_out, out
@@ -314,12 +331,14 @@ def fused_ar_rmsnorm(inputs, residual, weight, eps=1e-6, *, residual_out=None, o
         options: an Options (alternative kernel designs) or None for the defaults.
     Returns:
         (residual_out, out). Missing outputs are allocated with ``torch.empty_like(residual)``
-        and belong to the caller. The work is asynchronous on the stream.
+        (recorded on ``stream`` when one is given) and belong to the caller. The work is
+        asynchronous on the stream.
     Raises:
         TypeError/ValueError for tensors of the wrong dtype, device, shape or layout;
         FusedArError for a non-zero library status.
     """
-    m, hidden, device, residual_out, out = _prepare(inputs, residual, weight, residual_out, out)
+    m, hidden, device, residual_out, out = _prepare(inputs, residual, weight, residual_out, out,
+                                                    stream)
     n = len(inputs)
     arr = (_VP * n)(*[x.data_ptr() for x in inputs])
     with _device_guard(device):
@@ -336,7 +355,8 @@ def fused_ar_unfused_rmsnorm(inputs, residual, weight, eps=1e-6, *, residual_out
                              stream=None):
     """The same result as fused_ar_rmsnorm, computed as three kernels (reduce, residual add,
     RMSNorm): the unfused baseline. Arguments and returns as fused_ar_rmsnorm (no path)."""
-    m, hidden, device, residual_out, out = _prepare(inputs, residual, weight, residual_out, out)
+    m, hidden, device, residual_out, out = _prepare(inputs, residual, weight, residual_out, out,
+                                                    stream)
     with _device_guard(device):
         rc = fused_ar_unfused_rmsnorm_ptrs([x.data_ptr() for x in inputs], residual.data_ptr(),
                                            weight.data_ptr(), eps, m, hidden,
@@ -360,7 +380,7 @@ def fused_ar_reduce(inputs, *, reduced=None, stream=None):
     for i, x in enumerate(inputs):
         _check_tensor(x, f"inputs[{i}]", (m, hidden), x0.device)
     if reduced is None:
-        reduced = torch.empty_like(x0)
+        reduced = _on_stream(torch.empty_like(x0), stream)
     _check_tensor(reduced, "reduced", (m, hidden), x0.device)
     with _device_guard(x0.device):
         rc = fused_ar_reduce_ptrs([x.data_ptr() for x in inputs], m, hidden, reduced.data_ptr(),
@@ -377,14 +397,12 @@ def fused_ar_rmsnorm_split(inputs, residual, weight, eps=1e-6, *, splits=0, work
     ``split_workspace_bytes(m, hidden, splits)`` bytes, allocated here when None. Other arguments
     and returns as fused_ar_rmsnorm (always the one-stage path)."""
     import torch
-    m, hidden, device, residual_out, out = _prepare(inputs, residual, weight, residual_out, out)
+    m, hidden, device, residual_out, out = _prepare(inputs, residual, weight, residual_out, out,
+                                                    stream)
     need = split_workspace_bytes(m, hidden, splits)
     if workspace is None:
-        workspace = torch.empty(max(need, 4) // 4, dtype=torch.float32, device=device)
-        if stream is not None:
-            # allocated for the current stream but used on `stream`: keep the caching allocator
-            # from handing it out again before the work on `stream` is done
-            workspace.record_stream(stream)
+        workspace = _on_stream(torch.empty(max(need, 4) // 4, dtype=torch.float32, device=device),
+                               stream)
     if not isinstance(workspace, torch.Tensor) or workspace.device != device:
         raise ValueError(f"workspace must be a tensor on {device}")
     if not workspace.is_contiguous():

@@ -686,7 +686,26 @@ int resolve_path(int n, int m, int hidden, int path)
 
 }  // namespace
 
+// The automatic path on one GPU, from a sweep of both paths over n = 2..8, hidden = 2880..32768
+// and m = 1..8192 (MI355X, graphs of calls for cache-sized problems, HBM-cold loops above): the
+// one-stage path is faster everywhere (by 6 % to 2.8x) except where a few rows are each too long
+// for one CU: with at most kTwoStageMaxM rows that each read at least kTwoStageRowBytes (the n
+// inputs and the residual), the two-stage path's flat stage 1 spreads the reads over every CU and
+// wins by 2-16 % (e.g. n = 8, hidden = 32768, m = 1: 6.5 against 7.8 us). The thresholds of the
+// pages (fused_ar_auto_path_tp) weigh the link traffic between GPUs, which one GPU does not have.
+constexpr int kTwoStageMaxM = 16;
+constexpr uint64_t kTwoStageRowBytes = 432u * 1024u;
+
 extern "C" int fused_ar_auto_path(int n, int m, int hidden)
+{
+    if (n < 1 || n > FUSED_AR_MAX_INPUTS || m < 0 || hidden <= 0)
+        return FUSED_AR_ERR_INVALID;
+    const uint64_t row_read = 2ull * (uint64_t)(n + 1) * (uint64_t)hidden;
+    return (m <= kTwoStageMaxM && row_read >= kTwoStageRowBytes) ? FUSED_AR_PATH_TWOSTAGE
+                                                                  : FUSED_AR_PATH_ONESTAGE;
+}
+
+extern "C" int fused_ar_auto_path_tp(int n, int m, int hidden)
 {
     (void)hidden;
     if (n < 1 || n > FUSED_AR_MAX_INPUTS || m < 0)

@@ -69,6 +69,12 @@ def parse_args():
     ap.add_argument("--path-sweep", action="store_true",
                     help="only compare path 1 with path 2 over n in {2, 4, 8}, six row widths and "
                          "row counts 1..8192: one JSON line per shape (the one-GPU path rule)")
+    ap.add_argument("--sweep-n", type=str, default=None,
+                    help="--path-sweep: comma-separated input counts instead of the default grid")
+    ap.add_argument("--sweep-hidden", type=str, default=None,
+                    help="--path-sweep: comma-separated row widths instead of the default grid")
+    ap.add_argument("--sweep-m", type=str, default=None,
+                    help="--path-sweep: comma-separated row counts instead of the default grid")
     ap.add_argument("--chunk-sweep", action="store_true",
                     help="only time the two-stage path whole and in row chunks (sequential and "
                          "pipelined) on the HBM-cold shapes: one JSON line per shape")
@@ -464,13 +470,13 @@ PATH_SWEEP_HIDDEN = (2880, 4096, 7168, 8192, 16384, 32768)
 PATH_SWEEP_M = (1, 2, 8, 16, 17, 32, 33, 64, 256, 1024, 2048, 4096, 8192)
 
 
-def path_sweep(torch, fa):
+def path_sweep(torch, fa, ns=PATH_SWEEP_N, hiddens=PATH_SWEEP_HIDDEN, ms=PATH_SWEEP_M):
     """Path 1 against path 2 on one GPU over n x row width x row count (timing_for; the buffers
     are filled on the GPU). One JSON line per shape; shapes whose buffers exceed 3 GiB are
     skipped."""
-    for n in PATH_SWEEP_N:
-        for hidden in PATH_SWEEP_HIDDEN:
-            for m in PATH_SWEEP_M:
+    for n in ns:
+        for hidden in hiddens:
+            for m in ms:
                 footprint = 2 * (n + 3) * m * hidden
                 if footprint > (3 << 30):
                     continue
@@ -597,7 +603,10 @@ def main():
         all_workloads(torch, fa, synth, oracle)
         return
     if args.path_sweep:
-        path_sweep(torch, fa)
+        def grid(text, default):
+            return tuple(int(v) for v in text.split(",")) if text else default
+        path_sweep(torch, fa, grid(args.sweep_n, PATH_SWEEP_N),
+                   grid(args.sweep_hidden, PATH_SWEEP_HIDDEN), grid(args.sweep_m, PATH_SWEEP_M))
         return
     if args.chunk_sweep:
         chunk_sweep(torch, fa)

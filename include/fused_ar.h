@@ -229,13 +229,26 @@ int fused_ar_reduce(const fa_bf16 *const *inputs, int n, int m, int hidden, fa_b
                     hipStream_t stream);
 
 /*
- * fused_ar_auto_path - the path FUSED_AR_PATH_AUTO takes: one-stage for m <= 32 when n <= 4 and
- * for m <= 16 when n > 4, two-stage above (the selection thresholds that aiter PR #3817, Test
- * Results, quotes for TP4 and TP8, extended to other n by n <= 4 / n > 4).
- * Returns 1 or 2, or FUSED_AR_ERR_INVALID for n outside [1, 8] or m < 0. `hidden` is not used
- * by the current rule.
+ * fused_ar_auto_path - the path FUSED_AR_PATH_AUTO takes, tuned on one MI355X where all n partial
+ * sums are in local HBM: the two-stage path when m <= 16 and each row reads at least 432 KiB
+ * (2 (n + 1) hidden bytes: n inputs and the residual), the one-stage path otherwise. Measured over
+ * n = 2..8, hidden = 2880..32768, m = 1..8192: the one-stage path is faster everywhere except for
+ * a few rows too long for one CU each (from n = 8, hidden >= 24576 or n = 6, hidden = 32768 at
+ * m <= 16), where the two-stage path's flat first kernel spreads the reads over every CU.
+ * Returns 1 or 2, or FUSED_AR_ERR_INVALID for n outside [1, 8], m < 0 or hidden <= 0.
  */
 int fused_ar_auto_path(int n, int m, int hidden);
+
+/*
+ * fused_ar_auto_path_tp - the selection rule of the pages for a tensor-parallel group whose
+ * partial sums sit on n GPUs: one-stage for m <= 32 when n <= 4 and for m <= 16 when n > 4,
+ * two-stage above (aiter PR #3817, Test Results: the thresholds for TP4 and TP8, extended to other
+ * n by n <= 4 / n > 4). Those thresholds weigh the link traffic of reading every peer in full
+ * (one-stage) against a reduce-scatter and gather (two-stage), which one GPU does not have; the
+ * rule is kept for the multi-GPU form of this path. Returns 1 or 2, or FUSED_AR_ERR_INVALID for n
+ * outside [1, 8] or m < 0 (`hidden` is not used).
+ */
+int fused_ar_auto_path_tp(int n, int m, int hidden);
 
 /* One kernel launch of a call, as fused_ar_describe_launch reports it. */
 typedef struct {

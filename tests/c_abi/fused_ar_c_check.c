@@ -33,9 +33,15 @@ static const fa_bf16 *fake(uintptr_t i) { return (const fa_bf16 *)(0x7F000000000
 static int cpu_checks(void)
 {
     CHECK(fused_ar_auto_path(8, 16, 7168) == FUSED_AR_PATH_ONESTAGE);
-    CHECK(fused_ar_auto_path(8, 17, 7168) == FUSED_AR_PATH_TWOSTAGE);
-    CHECK(fused_ar_auto_path(4, 32, 7168) == FUSED_AR_PATH_ONESTAGE);
+    CHECK(fused_ar_auto_path(8, 4096, 7168) == FUSED_AR_PATH_ONESTAGE);
+    CHECK(fused_ar_auto_path(8, 16, 32768) == FUSED_AR_PATH_TWOSTAGE);
+    CHECK(fused_ar_auto_path(8, 17, 32768) == FUSED_AR_PATH_ONESTAGE);
     CHECK(fused_ar_auto_path(0, 1, 7168) == FUSED_AR_ERR_INVALID);
+    CHECK(fused_ar_auto_path(8, 1, 0) == FUSED_AR_ERR_INVALID);
+    CHECK(fused_ar_auto_path_tp(8, 16, 7168) == FUSED_AR_PATH_ONESTAGE);
+    CHECK(fused_ar_auto_path_tp(8, 17, 7168) == FUSED_AR_PATH_TWOSTAGE);
+    CHECK(fused_ar_auto_path_tp(4, 32, 7168) == FUSED_AR_PATH_ONESTAGE);
+    CHECK(fused_ar_auto_path_tp(0, 1, 7168) == FUSED_AR_ERR_INVALID);
 
     fused_ar_launch_plan plan;
     CHECK(fused_ar_describe_launch(8, 4096, 7168, FUSED_AR_PATH_ONESTAGE, &plan) == FUSED_AR_OK);

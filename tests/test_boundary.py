@@ -31,6 +31,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     assert {"fused_ar_rmsnorm", "fused_ar_rmsnorm_ex", "fused_ar_unfused_rmsnorm",
             "fused_ar_rmsnorm_check", "fused_ar_reduce", "fused_ar_auto_path",
+            "fused_ar_auto_path_tp",
             "fused_ar_describe_launch", "fused_ar_describe_launch_ex",
             "fused_ar_strerror"} <= set(names)
 
@@ -143,16 +144,39 @@ def test_reduce_checks():
     assert fa.fused_ar_reduce_ptrs(ins, 8, 16, addr(3), 0) == fa.ERR_ALIAS
 
 
+def one_gpu_path(n, m, hidden):
+    """The documented one-GPU rule: two-stage for at most 16 rows that each read at least 432 KiB
+    (n inputs and the residual), one-stage otherwise."""
+    return fa.PATH_TWOSTAGE if m <= 16 and 2 * (n + 1) * hidden >= 432 * 1024 else fa.PATH_ONESTAGE
+
+
 def test_auto_path_rule():
-    # One-stage up to m = 32 for n <= 4 and up to m = 16 for n > 4.
+    for n in range(1, 9):
+        for hidden in (8, 2880, 4096, 7168, 16384, 24568, 24576, 27648, 31592, 31600, 32768):
+            for m in (0, 1, 15, 16, 17, 32, 33, 4096):
+                assert fa.auto_path(n, m, hidden) == one_gpu_path(n, m, hidden), (n, m, hidden)
+    # the rule's corners: at n = 8 a row of 24576 reads exactly 432 KiB
+    assert fa.auto_path(8, 16, 24576) == fa.PATH_TWOSTAGE
+    assert fa.auto_path(8, 16, 24568) == fa.PATH_ONESTAGE
+    assert fa.auto_path(8, 17, 32768) == fa.PATH_ONESTAGE
+    assert fa.auto_path(4, 1, 32768) == fa.PATH_ONESTAGE    # 320 KiB per row
+    assert fa.auto_path(6, 1, 31600) == fa.PATH_TWOSTAGE
+    assert fa.auto_path(6, 1, 31592) == fa.PATH_ONESTAGE
+    for bad in ((0, 1, 4096), (9, 1, 4096), (4, -1, 4096), (4, 1, 0), (4, 1, -8)):
+        assert fa.auto_path(*bad) == fa.ERR_INVALID, bad
+
+
+def test_pages_path_rule_for_tensor_parallel_groups():
+    # One-stage up to m = 32 for n <= 4 and up to m = 16 for n > 4, whatever the row width.
     for n in range(1, 9):
         limit = 32 if n <= 4 else 16
-        assert fa.auto_path(n, 0, 4096) == fa.PATH_ONESTAGE
-        assert fa.auto_path(n, limit, 4096) == fa.PATH_ONESTAGE
-        assert fa.auto_path(n, limit + 1, 4096) == fa.PATH_TWOSTAGE
-    assert fa.auto_path(0, 1, 4096) == fa.ERR_INVALID
-    assert fa.auto_path(9, 1, 4096) == fa.ERR_INVALID
-    assert fa.auto_path(4, -1, 4096) == fa.ERR_INVALID
+        for hidden in (4096, 32768):
+            assert fa.auto_path_tp(n, 0, hidden) == fa.PATH_ONESTAGE
+            assert fa.auto_path_tp(n, limit, hidden) == fa.PATH_ONESTAGE
+            assert fa.auto_path_tp(n, limit + 1, hidden) == fa.PATH_TWOSTAGE
+    assert fa.auto_path_tp(0, 1, 4096) == fa.ERR_INVALID
+    assert fa.auto_path_tp(9, 1, 4096) == fa.ERR_INVALID
+    assert fa.auto_path_tp(4, -1, 4096) == fa.ERR_INVALID
 
 
 @pytest.mark.parametrize("hidden", [8, 512, 520, 2880, 4096, 7168, 8192, 8200, 16384, 32768])
@@ -200,8 +224,9 @@ def test_launch_geometry_by_row_count():
 
 
 def test_launch_geometry_auto_and_empty():
-    assert fa.describe_launch(8, 16, 7168)["path"] == 1
-    assert fa.describe_launch(8, 17, 7168)["path"] == 2
+    assert fa.describe_launch(8, 17, 7168)["path"] == 1
+    assert fa.describe_launch(8, 16, 32768)["path"] == 2
+    assert fa.describe_launch(8, 17, 32768)["path"] == 1
     assert fa.describe_launch(4, 0, 7168, 1)["kernels"] == []
     with pytest.raises(fa.FusedArError):
         fa.describe_launch(4, 8, 12, 1)

@@ -159,7 +159,8 @@ def check_plan(n, m, packs, path, wave, stage1, block, ppt, policy, rows=0, sche
         assert e.value.status == fa.ERR_SHAPE
         return
     plan = fa.describe_launch(n, m, hidden, path, opt)
-    want_path = path if path else (1 if m <= (32 if n <= 4 else 16) else 2)
+    # automatic: two-stage for at most 16 rows that each read at least 432 KiB, else one-stage
+    want_path = path if path else (2 if m <= 16 and 2 * (n + 1) * hidden >= 432 * 1024 else 1)
     assert plan["path"] == want_path
     if m == 0:
         assert plan["kernels"] == []

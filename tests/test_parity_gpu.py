@@ -127,12 +127,19 @@ def test_paths_agree_bit_for_bit():
 
 
 def test_auto_path_matches_explicit():
-    for n, m in [(8, 16), (8, 17), (4, 32), (4, 33)]:
-        p = synth.make_problem(n, m, 2880, seed=8)
-        announce(f"auto n={n} m={m}")
+    """The automatic path gives the bits of the path the rule names, on either side of the rule's
+    corners (two-stage only for a few rows of wide, many-input rows), and the oracle's result."""
+    for n, m, hidden in [(8, 16, 2880), (4, 33, 2880), (8, 16, 32768), (8, 17, 32768),
+                         (6, 3, 32768), (4, 3, 32768)]:
+        p = synth.make_problem(n, m, hidden, seed=8)
+        announce(f"auto n={n} m={m} hidden={hidden} -> path {fa.auto_path(n, m, hidden)}")
         r0 = run_gpu(p, 0)
-        r = run_gpu(p, fa.auto_path(n, m, 2880))
+        r = run_gpu(p, fa.auto_path(n, m, hidden))
         assert np.array_equal(r0[0], r[0]) and np.array_equal(r0[1], r[1])
+        want_ro, want_out = oracle_rows(p)
+        assert_parity(f"auto n={n} m={m} hidden={hidden}", r0[0], r0[1], want_ro, want_out)
+    assert fa.auto_path(8, 16, 32768) == fa.PATH_TWOSTAGE
+    assert fa.auto_path(8, 17, 32768) == fa.PATH_ONESTAGE
 
 
 # ------------------------------------------------------------------------- the reduce alone
@@ -454,6 +461,28 @@ def test_concurrent_calls_on_two_streams():
         want_ro, want_out = oracle_rows(p)
         for path, (ro, out) in outs.items():
             assert_parity(f"stream n={p.n} path={path}", host(ro), host(out), want_ro, want_out)
+
+
+def test_outputs_allocated_for_a_side_stream_are_not_reused_early():
+    """Outputs the binding allocates for work on a side stream are recorded on that stream: the
+    caller dropping them at once must not let the current stream's next allocation take their
+    memory while the side stream has not yet run the kernels that write them."""
+    p = synth.make_problem(8, 64, 7168, seed=24, name="side stream")
+    ins = [dev(x) for x in p.inputs]
+    res, w = dev(p.residual), dev(p.weight)
+    side = torch.cuda.Stream()  # default priority
+    torch.cuda.synchronize()
+    announce("outputs recorded on a side stream")
+    for path in (1, 2):
+        with torch.cuda.stream(side):
+            torch.cuda._sleep(20_000_000)  # keep the side stream busy for a few milliseconds
+        ro, out = fa.fused_ar_rmsnorm(ins, res, w, p.eps, path=path, stream=side)
+        taken = {ro.data_ptr(), out.data_ptr()}
+        del ro, out
+        fresh = [torch.empty_like(res) for _ in range(2)]  # the current stream's next blocks
+        assert not taken & {t.data_ptr() for t in fresh}, path
+        torch.cuda.synchronize()
+        del fresh
 
 
 # ------------------------------------------------------------------------- unfused baseline
