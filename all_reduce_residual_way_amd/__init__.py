@@ -15,10 +15,12 @@ import os
 __all__ = [
     "FusedArError", "Options", "library", "fused_ar_rmsnorm", "fused_ar_unfused_rmsnorm",
     "fused_ar_reduce", "fused_ar_rmsnorm_split", "split_workspace_bytes",
-    "fused_ar_rmsnorm_split_ptrs", "fused_ar_rmsnorm_ptrs", "fused_ar_rmsnorm_ex_ptrs",
+    "fused_ar_rmsnorm_split_ptrs", "fused_ar_rmsnorm_split_static",
+    "fused_ar_rmsnorm_split_static_ptrs", "fused_ar_rmsnorm_ptrs", "fused_ar_rmsnorm_ex_ptrs",
     "fused_ar_unfused_rmsnorm_ptrs", "fused_ar_reduce_ptrs", "fused_ar_rmsnorm_check_ptrs",
     "auto_path", "auto_path_tp", "describe_launch", "strerror",
-    "OK", "ERR_INVALID", "ERR_SHAPE", "ERR_ALIGN", "ERR_ALIAS",
+    "OK", "ERR_INVALID", "ERR_SHAPE", "ERR_ALIGN", "ERR_ALIAS", "ERR_SCRATCH",
+    "STATIC_SCRATCH_FLOATS",
     "PATH_AUTO", "PATH_ONESTAGE", "PATH_TWOSTAGE", "PATH_UNFUSED", "WAVE_DPP", "WAVE_BPERMUTE",
     "STAGE1_FLAT", "STAGE1_LDS", "LOAD_AUTO", "LOAD_CACHED", "LOAD_STREAM", "CHUNKS_AUTO",
     "CHUNKS_SEQUENTIAL", "CHUNKS_PIPELINED", "MAX_INPUTS",
@@ -28,13 +30,14 @@ __all__ = [
 LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfused_ar.so")
 
 # Values of include/fused_ar.h.
-OK, ERR_INVALID, ERR_SHAPE, ERR_ALIGN, ERR_ALIAS = 0, -1, -2, -3, -4
+OK, ERR_INVALID, ERR_SHAPE, ERR_ALIGN, ERR_ALIAS, ERR_SCRATCH = 0, -1, -2, -3, -4, -5
 PATH_AUTO, PATH_ONESTAGE, PATH_TWOSTAGE, PATH_UNFUSED = 0, 1, 2, 3
 WAVE_DPP, WAVE_BPERMUTE = 0, 1
 STAGE1_FLAT, STAGE1_LDS = 0, 1
 LOAD_AUTO, LOAD_CACHED, LOAD_STREAM = 0, 1, 2
 CHUNKS_AUTO, CHUNKS_SEQUENTIAL, CHUNKS_PIPELINED = 0, 1, 2
 MAX_INPUTS, MAX_HIDDEN = 8, 32768
+STATIC_SCRATCH_FLOATS = 65536
 
 _VP = ctypes.c_void_p
 
@@ -117,6 +120,10 @@ def library():
                                                ctypes.c_float, ctypes.c_int, ctypes.c_int, _VP,
                                                _VP, ctypes.c_int, _VP, ctypes.c_size_t, _VP]
         lib.fused_ar_rmsnorm_split.restype = ctypes.c_int
+        lib.fused_ar_rmsnorm_split_static.argtypes = [ctypes.POINTER(_VP), ctypes.c_int, _VP, _VP,
+                                                      ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                                      _VP, _VP, ctypes.c_int, _VP]
+        lib.fused_ar_rmsnorm_split_static.restype = ctypes.c_int
         lib.fused_ar_split_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
         lib.fused_ar_split_workspace_bytes.restype = ctypes.c_size_t
         lib.fused_ar_strerror.argtypes = [ctypes.c_int]
@@ -221,6 +228,17 @@ def fused_ar_rmsnorm_split_ptrs(input_ptrs, residual, weight, eps, m, hidden, re
                                             float(eps), int(m), int(hidden), _VP(residual_out),
                                             _VP(out), int(splits), _VP(workspace),
                                             int(workspace_bytes), _VP(stream))
+
+
+def fused_ar_rmsnorm_split_static_ptrs(input_ptrs, residual, weight, eps, m, hidden, residual_out,
+                                       out, splits=0, stream=0):
+    """Raw call of the split-row form that allocates nothing (its slice square-sums in the
+    library's static scratch); returns the status."""
+    arr = _ptr_array(input_ptrs)
+    return library().fused_ar_rmsnorm_split_static(arr, len(input_ptrs), _VP(residual),
+                                                   _VP(weight), float(eps), int(m), int(hidden),
+                                                   _VP(residual_out), _VP(out), int(splits),
+                                                   _VP(stream))
 
 
 _torch = None
@@ -416,4 +434,26 @@ def fused_ar_rmsnorm_split(inputs, residual, weight, eps=1e-6, *, splits=0, work
                                          _stream_handle(stream, device))
     if rc != OK:
         raise FusedArError(rc, "fused_ar_rmsnorm_split")
+    return residual_out, out
+
+
+def fused_ar_rmsnorm_split_static(inputs, residual, weight, eps=1e-6, *, splits=0,
+                                  residual_out=None, out=None, stream=None):
+    """fused_ar_rmsnorm_split with the slice square-sums in the library's static scratch instead of
+    a workspace: the library call allocates nothing (for callers that cannot allocate, e.g. under
+    graph capture; pass both outputs to allocate nothing here either). At most
+    STATIC_SCRATCH_FLOATS slice square-sums (m * slices) per call; calls on one GPU must not
+    overlap in time (they share the scratch). Other arguments and returns as
+    fused_ar_rmsnorm_split."""
+    m, hidden, device, residual_out, out = _prepare(inputs, residual, weight, residual_out, out,
+                                                    stream)
+    n = len(inputs)
+    arr = (_VP * n)(*[x.data_ptr() for x in inputs])
+    with _device_guard(device):
+        rc = library().fused_ar_rmsnorm_split_static(arr, n, residual.data_ptr(),
+                                                     weight.data_ptr(), eps, m, hidden,
+                                                     residual_out.data_ptr(), out.data_ptr(),
+                                                     int(splits), _stream_handle(stream, device))
+    if rc != OK:
+        raise FusedArError(rc, "fused_ar_rmsnorm_split_static")
     return residual_out, out

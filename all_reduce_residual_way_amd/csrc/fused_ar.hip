@@ -8,6 +8,9 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "kernels.h"
 
 namespace {
@@ -677,11 +680,91 @@ int execute(const Plan &plan, const fa_bf16 *const *inputs, int n, const fa_bf16
     return run_rows(plan.step[2], a, m, packs, stream);
 }
 
+// The two kernels of the split-row form over a validated call (m > 0), the slice square-sums in
+// `partial` (m * s floats of device memory).
+int run_split(const fa_bf16 *const *inputs, int n, const fa_bf16 *residual, const fa_bf16 *weight,
+              float eps, int m, int hidden, fa_bf16 *residual_out, fa_bf16 *out, int s,
+              int slice_packs, int threads, float *partial, hipStream_t stream)
+{
+    const int packs = hidden / kPackElems;
+    const bool stream_loads = use_stream(kDefaultOptions, n, m, hidden);
+    const void *reduce_kernel = stream_loads ? split_kernel_s<true>(n) : split_kernel_s<false>(n);
+    const void *norm_kernel = reinterpret_cast<const void *>(&fa::k_split_norm);
+    // rows in launches of at most kRowsPerLaunch, as for the row kernels
+    for (int64_t first = 0; first < m; first += kRowsPerLaunch) {
+        const int rows = static_cast<int>(m - first < kRowsPerLaunch ? m - first : kRowsPerLaunch);
+        const size_t skip = (size_t)first * (size_t)packs;  // in packs
+        fa::SplitArgs a{};
+        for (int i = 0; i < n; ++i)
+            a.r.in[i] = reinterpret_cast<const u32x4 *>(inputs[i]) + skip;
+        a.r.residual = reinterpret_cast<const u32x4 *>(residual) + skip;
+        a.r.weight = reinterpret_cast<const u32x4 *>(weight);
+        a.r.residual_out = reinterpret_cast<u32x4 *>(residual_out) + skip;
+        a.r.out = reinterpret_cast<u32x4 *>(out) + skip;
+        a.r.eps = eps;
+        a.r.inv_hidden = static_cast<float>(1.0 / hidden);
+        a.r.packs = packs;
+        a.r.tiny_eps = eps < 0x1p-126f;
+        a.partial = partial + (size_t)first * (size_t)s;
+        a.splits = s;
+        a.slice_packs = slice_packs;
+        const unsigned grid = static_cast<unsigned>(rows) * static_cast<unsigned>(s);
+        int rc = launch(reduce_kernel, grid, static_cast<unsigned>(threads), &a, stream);
+        if (rc != FUSED_AR_OK)
+            return rc;
+        rc = launch(norm_kernel, grid, static_cast<unsigned>(threads), &a, stream);
+        if (rc != FUSED_AR_OK)
+            return rc;
+    }
+    return FUSED_AR_OK;
+}
+
 int resolve_path(int n, int m, int hidden, int path)
 {
     if (path == FUSED_AR_PATH_UNFUSED)
         return kPathUnfusedPlan;
     return path == FUSED_AR_PATH_AUTO ? fused_ar_auto_path(n, m, hidden) : path;
+}
+
+}  // namespace
+
+// Slice square-sums of fused_ar_rmsnorm_split_static: a fixed device array, so that the call needs
+// no workspace and allocates nothing. Each GPU the library runs on holds its own copy until the
+// process ends. In host code `scratch` names a host-side stand-in, not device memory: the copy on
+// the current device is reached only through the address hipGetSymbolAddress returns for it, which
+// static_scratch() looks up once per device and keeps.
+static __device__ __align__(256) float scratch[FUSED_AR_STATIC_SCRATCH_FLOATS];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<float *> g_scratch[kMaxDevices];
+std::mutex g_scratch_lookup;
+
+// The device address of `scratch` on the current device: a HIP error code or FUSED_AR_OK.
+int static_scratch(float **ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return static_cast<int>(e);
+    if (dev < 0 || dev >= kMaxDevices)
+        return FUSED_AR_ERR_INVALID;
+    float *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> guard(g_scratch_lookup);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            void *q = nullptr;
+            e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+            if (e != hipSuccess)
+                return static_cast<int>(e);
+            p = static_cast<float *>(q);
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return FUSED_AR_OK;
 }
 
 }  // namespace
@@ -846,37 +929,33 @@ extern "C" int fused_ar_rmsnorm_split(const fa_bf16 *const *inputs, int n, const
     if (make_span(weight, (size_t)hidden * sizeof(fa_bf16), &other) && overlaps(ws, other))
         return FUSED_AR_ERR_ALIAS;
 
-    const int packs = hidden / kPackElems;
-    const bool stream_loads = use_stream(kDefaultOptions, n, m, hidden);
-    const void *reduce_kernel = stream_loads ? split_kernel_s<true>(n) : split_kernel_s<false>(n);
-    const void *norm_kernel = reinterpret_cast<const void *>(&fa::k_split_norm);
-    // rows in launches of at most kRowsPerLaunch, as for the row kernels
-    for (int64_t first = 0; first < m; first += kRowsPerLaunch) {
-        const int rows = static_cast<int>(m - first < kRowsPerLaunch ? m - first : kRowsPerLaunch);
-        const size_t skip = (size_t)first * (size_t)packs;  // in packs
-        fa::SplitArgs a{};
-        for (int i = 0; i < n; ++i)
-            a.r.in[i] = reinterpret_cast<const u32x4 *>(inputs[i]) + skip;
-        a.r.residual = reinterpret_cast<const u32x4 *>(residual) + skip;
-        a.r.weight = reinterpret_cast<const u32x4 *>(weight);
-        a.r.residual_out = reinterpret_cast<u32x4 *>(residual_out) + skip;
-        a.r.out = reinterpret_cast<u32x4 *>(out) + skip;
-        a.r.eps = eps;
-        a.r.inv_hidden = static_cast<float>(1.0 / hidden);
-        a.r.packs = packs;
-        a.r.tiny_eps = eps < 0x1p-126f;
-        a.partial = static_cast<float *>(workspace) + (size_t)first * (size_t)s;
-        a.splits = s;
-        a.slice_packs = slice_packs;
-        const unsigned grid = static_cast<unsigned>(rows) * static_cast<unsigned>(s);
-        rc = launch(reduce_kernel, grid, static_cast<unsigned>(threads), &a, stream);
-        if (rc != FUSED_AR_OK)
-            return rc;
-        rc = launch(norm_kernel, grid, static_cast<unsigned>(threads), &a, stream);
-        if (rc != FUSED_AR_OK)
-            return rc;
-    }
-    return FUSED_AR_OK;
+    return run_split(inputs, n, residual, weight, eps, m, hidden, residual_out, out, s, slice_packs,
+                     threads, static_cast<float *>(workspace), stream);
+}
+
+extern "C" int fused_ar_rmsnorm_split_static(const fa_bf16 *const *inputs, int n,
+                                             const fa_bf16 *residual, const fa_bf16 *weight,
+                                             float eps, int m, int hidden, fa_bf16 *residual_out,
+                                             fa_bf16 *out, int splits, hipStream_t stream)
+{
+    int rc = check_scalars(n, m, hidden, eps, FUSED_AR_PATH_ONESTAGE, true);
+    if (rc != FUSED_AR_OK)
+        return rc;
+    int s, slice_packs, threads;
+    rc = split_geometry(hidden, splits, &s, &slice_packs, &threads);
+    if (rc != FUSED_AR_OK || m == 0)
+        return rc;
+    rc = check_buffers(inputs, n, residual, weight, m, hidden, residual_out, out);
+    if (rc != FUSED_AR_OK)
+        return rc;
+    if ((uint64_t)m * (uint64_t)s > (uint64_t)FUSED_AR_STATIC_SCRATCH_FLOATS)
+        return FUSED_AR_ERR_SCRATCH;
+    float *partial = nullptr;
+    rc = static_scratch(&partial);
+    if (rc != FUSED_AR_OK)
+        return rc;
+    return run_split(inputs, n, residual, weight, eps, m, hidden, residual_out, out, s, slice_packs,
+                     threads, partial, stream);
 }
 
 extern "C" int fused_ar_describe_launch_ex(int n, int m, int hidden, int path,
@@ -930,6 +1009,9 @@ extern "C" const char *fused_ar_strerror(int status)
                "slice count asked for)";
     case FUSED_AR_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
     case FUSED_AR_ERR_ALIAS: return "forbidden overlap between output and other buffers";
+    case FUSED_AR_ERR_SCRATCH:
+        return "the call needs more slice square-sums (m * slices) than the library's static "
+               "scratch holds (FUSED_AR_STATIC_SCRATCH_FLOATS)";
     default: break;
     }
     if (status > 0)

@@ -51,7 +51,9 @@ enum {
                                   row (slice) that does not fit 1024 threads at the packs per
                                   thread (slices) a caller forced */
     FUSED_AR_ERR_ALIGN = -3,   /* a device pointer not 16-byte aligned */
-    FUSED_AR_ERR_ALIAS = -4    /* a forbidden overlap of buffers (see fused_ar_rmsnorm) */
+    FUSED_AR_ERR_ALIAS = -4,   /* a forbidden overlap of buffers (see fused_ar_rmsnorm) */
+    FUSED_AR_ERR_SCRATCH = -5  /* fused_ar_rmsnorm_split_static: m * slices above
+                                  FUSED_AR_STATIC_SCRATCH_FLOATS */
 };
 
 #define FUSED_AR_MAX_INPUTS 8
@@ -138,6 +140,32 @@ int fused_ar_rmsnorm_split(const fa_bf16 *const *inputs, int n, const fa_bf16 *r
 /* fused_ar_split_workspace_bytes - the workspace fused_ar_rmsnorm_split needs for these scalars
  * (m * slices * 4 bytes); 0 when m == 0 or the scalars are invalid. */
 size_t fused_ar_split_workspace_bytes(int m, int hidden, int splits);
+
+/* Floats in the library's static scratch (256 KiB per GPU): fused_ar_rmsnorm_split_static takes
+ * calls with m * slices up to this many. */
+#define FUSED_AR_STATIC_SCRATCH_FLOATS 65536
+
+/*
+ * fused_ar_rmsnorm_split_static - fused_ar_rmsnorm_split without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. The slice square-sums go to a fixed device array of the library,
+ * FUSED_AR_STATIC_SCRATCH_FLOATS floats, of which each GPU the library runs on holds its own copy
+ * until the process ends; the call itself allocates nothing (no hipMalloc, no hipFree). The first
+ * call on a device looks up that device's copy (hipGetSymbolAddress, with the device current).
+ *   Limit: m * slices <= FUSED_AR_STATIC_SCRATCH_FLOATS (slices as fused_ar_split_workspace_bytes
+ *   counts them: m <= 16384 at hidden 7168, m <= 4096 at hidden 32768, with the default slices);
+ *   larger calls return FUSED_AR_ERR_SCRATCH and launch nothing.
+ *   Sharing: every call on one GPU uses the same array, and it keeps the last call's contents
+ *   (each call writes every slot it reads before reading it, so nothing needs clearing). Calls on
+ *   one GPU that may run at the same time - on streams not ordered with one another - race on it
+ *   and must not be made; calls ordered on one stream are safe.
+ * Results are bit-identical to fused_ar_rmsnorm_split with the same arguments and splits. Other
+ * arguments, conventions and errors as for fused_ar_rmsnorm_split (no workspace checks).
+ */
+int fused_ar_rmsnorm_split_static(const fa_bf16 *const *inputs, int n, const fa_bf16 *residual,
+                                  const fa_bf16 *weight, float eps, int m, int hidden,
+                                  fa_bf16 *residual_out, fa_bf16 *out, int splits,
+                                  hipStream_t stream);
 
 /* Options of fused_ar_rmsnorm_ex: alternative kernel designs, for comparison and tuning. */
 enum {

@@ -47,7 +47,7 @@ def test_header_constants_match_binding():
         text = f.read()
     for name, value in [("FUSED_AR_OK", fa.OK), ("FUSED_AR_ERR_INVALID", fa.ERR_INVALID),
                         ("FUSED_AR_ERR_SHAPE", fa.ERR_SHAPE), ("FUSED_AR_ERR_ALIGN", fa.ERR_ALIGN),
-                        ("FUSED_AR_ERR_ALIAS", fa.ERR_ALIAS), ("FUSED_AR_PATH_AUTO", fa.PATH_AUTO),
+                        ("FUSED_AR_ERR_ALIAS", fa.ERR_ALIAS), ("FUSED_AR_ERR_SCRATCH", fa.ERR_SCRATCH), ("FUSED_AR_PATH_AUTO", fa.PATH_AUTO),
                         ("FUSED_AR_PATH_ONESTAGE", fa.PATH_ONESTAGE),
                         ("FUSED_AR_PATH_TWOSTAGE", fa.PATH_TWOSTAGE),
                         ("FUSED_AR_PATH_UNFUSED", fa.PATH_UNFUSED),
@@ -61,6 +61,7 @@ def test_header_constants_match_binding():
         assert re.search(rf"\b{name}\s*=\s*{value}\b", text), name
     assert re.search(rf"#define FUSED_AR_MAX_INPUTS {fa.MAX_INPUTS}\b", text)
     assert re.search(rf"#define FUSED_AR_MAX_HIDDEN {fa.MAX_HIDDEN}\b", text)
+    assert re.search(rf"#define FUSED_AR_STATIC_SCRATCH_FLOATS {fa.STATIC_SCRATCH_FLOATS}\b", text)
 
 
 def call(n=4, m=8, hidden=4096, eps=1e-6, path=1, inputs=None, residual=None, weight=None,
@@ -234,7 +235,7 @@ def test_launch_geometry_auto_and_empty():
 
 def test_strerror():
     assert fa.strerror(fa.OK) == "success"
-    for code in (fa.ERR_INVALID, fa.ERR_SHAPE, fa.ERR_ALIGN, fa.ERR_ALIAS):
+    for code in (fa.ERR_INVALID, fa.ERR_SHAPE, fa.ERR_ALIGN, fa.ERR_ALIAS, fa.ERR_SCRATCH):
         assert fa.strerror(code) and fa.strerror(code) != "unknown status"
     assert fa.strerror(-99) == "unknown status"
 
@@ -400,6 +401,42 @@ def test_split_workspace_and_slices():
     assert fa.split_workspace_bytes(1, 12) == 0            # hidden not a multiple of 8
     # m == 0: success before any pointer is looked at
     assert fa.fused_ar_rmsnorm_split_ptrs([0], 0, 0, 1e-6, 0, 4096, 0, 0, 0, 0, 0, 0) == fa.OK
+
+
+def static_split_call(n=4, m=8, hidden=4096, eps=1e-6, splits=0, **bufs):
+    ins = bufs.get("inputs", [addr(i) for i in range(n)])
+    return fa.fused_ar_rmsnorm_split_static_ptrs(
+        ins, bufs.get("residual", addr(10)), bufs.get("weight", addr(11)), eps, m, hidden,
+        bufs.get("residual_out", addr(12)), bufs.get("out", addr(13)), splits, 0)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(m=16385, hidden=7168), fa.ERR_SCRATCH),        # 4 slices: 65540 square-sums
+    (dict(m=1025, hidden=8192, splits=64), fa.ERR_SCRATCH),
+    (dict(m=4097, hidden=32768), fa.ERR_SCRATCH),        # 16 slices
+    (dict(m=(1 << 31) - 1, hidden=32768, splits=64), fa.ERR_ALIAS),  # planes overlap first
+    (dict(splits=65), fa.ERR_INVALID),
+    (dict(hidden=16384, splits=1), fa.ERR_SHAPE),
+    (dict(n=0), fa.ERR_INVALID),
+    (dict(eps=-1.0), fa.ERR_INVALID),
+    (dict(hidden=4100), fa.ERR_SHAPE),
+    (dict(out=addr(2)), fa.ERR_ALIAS),
+    (dict(residual_out=addr(12) + 8), fa.ERR_ALIGN),
+    (dict(weight=0), fa.ERR_INVALID),
+])
+def test_static_split_rejected_before_launch(kwargs, code):
+    """The static-scratch split call checks like the workspace form, then rejects calls whose slice
+    square-sums exceed the static scratch, all before any HIP call."""
+    assert static_split_call(**kwargs) == code
+
+
+def test_static_split_limit_and_empty_call():
+    # m == 0: success with nothing looked at; the limit is m * slices, slices as the workspace
+    # form counts them
+    assert static_split_call(m=0, inputs=[0], residual=0, weight=0, residual_out=0, out=0) == fa.OK
+    assert fa.split_workspace_bytes(16384, 7168) == 4 * fa.STATIC_SCRATCH_FLOATS
+    assert fa.split_workspace_bytes(4096, 32768) == 4 * fa.STATIC_SCRATCH_FLOATS
+    assert "static scratch" in fa.strerror(fa.ERR_SCRATCH)
 
 
 def test_launch_plan_struct_matches_header():
