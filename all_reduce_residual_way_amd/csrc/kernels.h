@@ -92,6 +92,12 @@ __device__ __forceinline__ u32x4 normalise(const F8 &y, const F8 &g, float rstd)
     return narrow(o);
 }
 
+// Below this fp32 square-sum a row's squares may have lost bits to the subnormal range (each
+// y * y under 2^-126 is rounded to a multiple of 2^-149), enough to move `out` past its 1-ulp band:
+// with eps below the normal range the row kernel then sums the squares again at a 2^100 scale.
+// Above it those roundings add at most hidden * 2^-150 < 2^-135, under 2^-25 of the sum.
+constexpr float kTinySquareSum = 0x1p-110f;
+
 // 1 / sqrt(v) for v = mean + eps >= eps by the hardware reciprocal square root (v_rsq_f32, within
 // 1 ulp in fp32). Below the normal range v is scaled by 2^24 first (and the result by 2^12), so
 // subnormal arguments keep the same accuracy; 0 gives +inf. They are possible only when eps itself
@@ -240,7 +246,28 @@ __device__ __forceinline__ void row_pass(const RowArgs &a, float eps, float inv_
     }
 
     const float total = block_sum<kBpermute>(ss, slots);
-    const float rstd = rsqrt_f32(total * inv_hidden + eps, tiny_eps);
+    float rstd = rsqrt_f32(total * inv_hidden + eps, tiny_eps);
+    if (tiny_eps && total < kTinySquareSum) {
+        // eps = 0 or subnormal and a row so small that squares below 2^-126 lost bits or vanished:
+        // the square-sum again over x * 2^100 (exact scaling, squares exact and normal), mean + eps
+        // scaled by 2^200 likewise, and the reciprocal root scaled back by 2^100. A uniform branch
+        // (tiny_eps and total are the same in every wave); the second sum has LDS of its own.
+        __shared__ float slots_scaled[kMaxWaves];
+        float ss2 = 0.0f;
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
+            if (tid + k * nthreads < packs) {
+                const F8 y = PPT == 1 ? y1 : widen(ro[k]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float z = y.v[e] * 0x1p100f;
+                    ss2 = __builtin_fmaf(z, z, ss2);
+                }
+            }
+        }
+        const float total2 = block_sum<kBpermute>(ss2, slots_scaled);
+        rstd = 0x1p100f * __builtin_amdgcn_rsqf(total2 * inv_hidden + eps * 0x1p100f * 0x1p100f);
+    }
 
 #pragma unroll
     for (int k = 0; k < PPT; ++k) {
@@ -410,7 +437,25 @@ __global__ void __launch_bounds__(1024) k_split_norm(SplitArgs a)
     float total = lane_value(mine, 0);
     for (uint32_t i = 1; i < splits; ++i)
         total = total + lane_value(mine, (int)i);
-    const float rstd = rsqrt_f32(total * a.r.inv_hidden + a.r.eps, a.r.tiny_eps);
+    float rstd = rsqrt_f32(total * a.r.inv_hidden + a.r.eps, a.r.tiny_eps);
+    if (a.r.tiny_eps && total < kTinySquareSum) {
+        // as in row_pass: the square-sum again at a 2^100 scale, here over the whole row's
+        // residual_out (written by k_split_reduce), in the same order in every workgroup of the
+        // row; a uniform branch, since every workgroup of the row holds the same total
+        __shared__ float slots[kMaxWaves];
+        const char *row_ro = reinterpret_cast<const char *>(a.r.residual_out) + row_bytes;
+        float ss2 = 0.0f;
+        for (uint32_t q = threadIdx.x; q < packs; q += blockDim.x) {
+            const F8 y = widen(load_pack(row_ro, q * (uint32_t)sizeof(u32x4)));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float z = y.v[e] * 0x1p100f;
+                ss2 = __builtin_fmaf(z, z, ss2);
+            }
+        }
+        const float total2 = block_sum<false>(ss2, slots);
+        rstd = 0x1p100f * __builtin_amdgcn_rsqf(total2 * a.r.inv_hidden + a.r.eps * 0x1p100f * 0x1p100f);
+    }
     if (active)
         store_stream(reinterpret_cast<char *>(a.r.out) + row_bytes, off,
                      normalise(widen(yv), widen(gv), rstd));

@@ -78,7 +78,11 @@ enum {
  *   residual      device [m, hidden] bf16.
  *   weight        device [hidden] bf16.
  *   eps           >= 0 and finite; added to the mean of squares inside the square root. With
- *                 eps == 0 a row that is all zero gives NaN (0 * inf), as the formula does.
+ *                 eps == 0 a row that is all zero gives NaN (0 * inf), as the formula does. With
+ *                 eps below 2^-126 (0 or subnormal), rows so small that their fp32 square-sum is
+ *                 below 2^-110 are summed again at a 2^100 scale, so that squares in or under
+ *                 fp32's subnormal range keep their bits. The statistic is fp32: rows whose
+ *                 square-sum exceeds fp32's range (|x| above about 1.8e19) give out = 0.
  *   m, hidden     rows (tokens) and row length; m == 0 returns FUSED_AR_OK and launches nothing
  *                 (no pointer is looked at); hidden % 8 == 0 and hidden <= FUSED_AR_MAX_HIDDEN.
  *   residual_out  device [m, hidden] bf16, written. May be exactly `residual` (in place); it must

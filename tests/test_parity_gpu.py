@@ -254,19 +254,27 @@ def test_eps_values(eps):
 
 @pytest.mark.parametrize("eps", [0.0, 1e-44, 2.0 ** -126])
 def test_tiny_rows_with_subnormal_mean_square(eps):
-    """Rows scaled by 2^-60 .. 2^-68, so that mean(x^2) + eps falls from the normal range (1e-36)
-    into fp32's subnormals (down to 3e-41) with eps = 0 or subnormal: the reciprocal square root
-    must stay accurate there. With eps = 2^-126, the smallest normal value, mean + eps stays normal
-    although the mean is subnormal, and the kernel takes its unscaled form."""
+    """Rows scaled by 2^-60 .. 2^-120, so that mean(x^2) falls from the normal range (1e-36) through
+    fp32's subnormals to far below them, with eps = 0 or subnormal: the kernels sum such rows'
+    squares again at a 2^100 scale (squares below 2^-126 lose bits, below 2^-149 vanish), so out
+    stays within 1 ulp of the oracle instead of turning into +-inf. With eps = 2^-126, the smallest
+    normal value, eps dominates mean + eps and the kernel takes its unscaled form. Every path and
+    the split-row form."""
     rng = np.random.default_rng(31)
-    scales = [2.0 ** -60, 2.0 ** -63, 2.0 ** -66, 2.0 ** -68]
+    scales = [2.0 ** -60, 2.0 ** -63, 2.0 ** -66, 2.0 ** -68, 2.0 ** -72, 2.0 ** -80,
+              2.0 ** -100, 2.0 ** -120]
     inputs = [synth.to_bf16_bits(np.array([rng.standard_normal(64) * s for s in scales],
                                           dtype=np.float32)) for _ in range(2)]
     residual = np.zeros((len(scales), 64), dtype=np.uint16)
     weight = synth.to_bf16_bits((1 + 0.1 * rng.standard_normal(64)).astype(np.float32))
     p = synth.Problem(inputs, residual, weight, eps, name=f"tiny rows eps={eps}")
-    for path in (1, 2):
+    for path in (1, 2, fa.PATH_UNFUSED):
         check_problem(p, path)
+    want_ro, want_out = oracle_rows(p)
+    for splits in (1, 3):
+        announce(f"tiny rows eps={eps} split rows splits={splits}")
+        ro, out = run_split(p, splits)
+        assert_parity(f"tiny rows split {splits}", ro, out, want_ro, want_out)
 
 
 def test_large_values_and_ties():
