@@ -23,7 +23,8 @@ __all__ = [
     "STATIC_SCRATCH_FLOATS",
     "PATH_AUTO", "PATH_ONESTAGE", "PATH_TWOSTAGE", "PATH_UNFUSED", "WAVE_DPP", "WAVE_BPERMUTE",
     "STAGE1_FLAT", "STAGE1_LDS", "LOAD_AUTO", "LOAD_CACHED", "LOAD_STREAM", "CHUNKS_AUTO",
-    "CHUNKS_SEQUENTIAL", "CHUNKS_PIPELINED", "MAX_INPUTS",
+    "CHUNKS_SEQUENTIAL", "CHUNKS_PIPELINED", "RESIDUAL_AUTO", "RESIDUAL_STAGE2", "RESIDUAL_STAGE1",
+    "MAX_INPUTS",
     "MAX_HIDDEN",
 ]
 
@@ -36,6 +37,7 @@ WAVE_DPP, WAVE_BPERMUTE = 0, 1
 STAGE1_FLAT, STAGE1_LDS = 0, 1
 LOAD_AUTO, LOAD_CACHED, LOAD_STREAM = 0, 1, 2
 CHUNKS_AUTO, CHUNKS_SEQUENTIAL, CHUNKS_PIPELINED = 0, 1, 2
+RESIDUAL_AUTO, RESIDUAL_STAGE2, RESIDUAL_STAGE1 = 0, 1, 2
 MAX_INPUTS, MAX_HIDDEN = 8, 32768
 STATIC_SCRATCH_FLOATS = 65536
 
@@ -57,7 +59,7 @@ class Options(ctypes.Structure):
     _fields_ = [("wave_reduce", ctypes.c_int), ("stage1", ctypes.c_int),
                 ("stage1_block", ctypes.c_int), ("packs_per_thread", ctypes.c_int),
                 ("load_policy", ctypes.c_int), ("stage_rows", ctypes.c_int),
-                ("schedule", ctypes.c_int)]
+                ("schedule", ctypes.c_int), ("residual_stage", ctypes.c_int)]
 
 
 class FusedArError(RuntimeError):

@@ -115,10 +115,11 @@ struct Options {
     int load_policy;      // FUSED_AR_LOAD_AUTO, _CACHED or _STREAM
     int stage_rows;       // two-stage path: rows per chunk; 0 = automatic, -1 = one chunk
     int schedule;         // FUSED_AR_CHUNKS_AUTO, _SEQUENTIAL or _PIPELINED
+    int residual_stage;   // two-stage path: FUSED_AR_RESIDUAL_AUTO, _STAGE2 or _STAGE1
 };
 
 constexpr Options kDefaultOptions = {false, false, 0, 0, FUSED_AR_LOAD_AUTO, 0,
-                                     FUSED_AR_CHUNKS_AUTO};
+                                     FUSED_AR_CHUNKS_AUTO, FUSED_AR_RESIDUAL_AUTO};
 
 unsigned flat_block_for(const Options &o, size_t total_packs)
 {
@@ -164,6 +165,13 @@ int read_options(const fused_ar_options *o, Options *out)
     if (o->schedule != FUSED_AR_CHUNKS_AUTO && o->schedule != FUSED_AR_CHUNKS_SEQUENTIAL &&
         o->schedule != FUSED_AR_CHUNKS_PIPELINED)
         return FUSED_AR_ERR_INVALID;
+    if (o->residual_stage != FUSED_AR_RESIDUAL_AUTO &&
+        o->residual_stage != FUSED_AR_RESIDUAL_STAGE2 && o->residual_stage != FUSED_AR_RESIDUAL_STAGE1)
+        return FUSED_AR_ERR_INVALID;
+    // the residual add in stage 1 has only the flat, unchunked form
+    if (o->residual_stage == FUSED_AR_RESIDUAL_STAGE1 &&
+        (o->stage1 == FUSED_AR_STAGE1_LDS || o->stage_rows > 0))
+        return FUSED_AR_ERR_INVALID;
     out->bpermute = o->wave_reduce == FUSED_AR_WAVE_BPERMUTE;
     out->lds_stage1 = o->stage1 == FUSED_AR_STAGE1_LDS;
     out->flat_block = static_cast<unsigned>(o->stage1_block);
@@ -171,6 +179,7 @@ int read_options(const fused_ar_options *o, Options *out)
     out->load_policy = o->load_policy;
     out->stage_rows = o->stage_rows;
     out->schedule = o->schedule;
+    out->residual_stage = o->residual_stage;
     return FUSED_AR_OK;
 }
 
@@ -278,6 +287,27 @@ const void *flat_kernel_s(int n)
 const void *flat_kernel(int n, bool stream)
 {
     return stream ? flat_kernel_s<true>(n) : flat_kernel_s<false>(n);
+}
+
+template <bool kS>
+const void *flat_residual_kernel_s(int n)
+{
+    switch (n) {
+    case 1: return reinterpret_cast<const void *>(&fa::k_flat_residual<1, kS>);
+    case 2: return reinterpret_cast<const void *>(&fa::k_flat_residual<2, kS>);
+    case 3: return reinterpret_cast<const void *>(&fa::k_flat_residual<3, kS>);
+    case 4: return reinterpret_cast<const void *>(&fa::k_flat_residual<4, kS>);
+    case 5: return reinterpret_cast<const void *>(&fa::k_flat_residual<5, kS>);
+    case 6: return reinterpret_cast<const void *>(&fa::k_flat_residual<6, kS>);
+    case 7: return reinterpret_cast<const void *>(&fa::k_flat_residual<7, kS>);
+    case 8: return reinterpret_cast<const void *>(&fa::k_flat_residual<8, kS>);
+    default: return nullptr;
+    }
+}
+
+const void *flat_residual_kernel(int n, bool stream)
+{
+    return stream ? flat_residual_kernel_s<true>(n) : flat_residual_kernel_s<false>(n);
 }
 
 template <int P, bool kS>
@@ -388,7 +418,21 @@ struct Plan {
     int chunk_rows;  // two-stage path: rows per chunk (m: one chunk)
     bool pipelined;  // two-stage path in chunks: stage 2 of a chunk and stage 1 of the next share
                      // a launch (k_pipe)
+    bool stage1_residual;  // two-stage path with the residual add in stage 1
 };
+
+// Where the two-stage path adds the residual. In stage 1 unless the caller asks for the pages'
+// split, or for a form that exists only with it (the LDS-staged stage 1, chunks of rows): then
+// stage 1 stores the reduced rows into `out` and stage 2 reads them back and adds the residual.
+// Measured on MI355X (HBM-cold, bit-identical results): n = 4, m = 4096, hidden 7168 86.5 ->
+// 78.0 us; n = 8, 8192 x 8192 274.5 -> 256.6 us; n = 8, m = 4096, hidden 7168 126.8 -> 117.5 us:
+// one plane less read and one less written.
+bool residual_in_stage1(const Options &o)
+{
+    if (o.residual_stage != FUSED_AR_RESIDUAL_AUTO)
+        return o.residual_stage == FUSED_AR_RESIDUAL_STAGE1;
+    return !o.lds_stage1 && o.stage_rows <= 0;
+}
 
 // Rows per chunk of the two-stage path, and whether the chunks are pipelined.
 int chunk_rows_for(const Options &o, int m)
@@ -457,6 +501,18 @@ int make_plan(int n, int m, int hidden, int path, const Options &o, Plan *plan)
                                   flat_block_for(o, total), stream);
     }
     rows.n = 1;
+    if (path == FUSED_AR_PATH_TWOSTAGE && residual_in_stage1(o)) {
+        // stage 1 writes residual_out; stage 2 is the plain RMSNorm of it
+        plan->stage1_residual = true;
+        plan->chunk_rows = m;
+        plan->step[0] = flat_step(flat_residual_kernel(n, stream), "stage1_reduce_residual", n,
+                                  total, flat_block_for(o, total), stream);
+        rows.kernel = row_kernel(1, ppt, o.bpermute, false, stream);
+        rows.name = "stage2_rmsnorm";
+        plan->steps = 2;
+        plan->step[1] = rows;
+        return FUSED_AR_OK;
+    }
     if (path == FUSED_AR_PATH_TWOSTAGE) {
         rows.kernel = row_kernel(1, ppt, o.bpermute, true, stream);
         rows.name = "stage2_norm";
@@ -631,6 +687,27 @@ int run_chunks(const Plan &plan, const u32x4 *const *ins, int n, const RowArgs &
     return stage2(first, m - first);
 }
 
+// The residual-adding stage 1 (k_flat_residual) over total_packs packs, in launches of at most
+// kFlatPacksPerLaunch packs as run_flat.
+int run_flat_residual(const Step &s, const u32x4 *const *inputs, const u32x4 *residual,
+                      size_t total_packs, u32x4 *residual_out, hipStream_t stream)
+{
+    for (size_t first = 0; first < total_packs; first += kFlatPacksPerLaunch) {
+        const size_t left = total_packs - first;
+        fa::FlatResidualArgs a{};
+        for (int i = 0; i < s.n; ++i)
+            a.f.in[i] = inputs[i] + first;
+        a.f.out = residual_out + first;
+        a.f.packs = static_cast<uint32_t>(left < kFlatPacksPerLaunch ? left : kFlatPacksPerLaunch);
+        a.residual = residual + first;
+        const unsigned grid = (a.f.packs + s.block - 1) / s.block;
+        const int rc = launch(s.kernel, grid, s.block, &a, stream);
+        if (rc != FUSED_AR_OK)
+            return rc;
+    }
+    return FUSED_AR_OK;
+}
+
 // Runs a validated call (m > 0) along `plan`.
 int execute(const Plan &plan, const fa_bf16 *const *inputs, int n, const fa_bf16 *residual,
             const fa_bf16 *weight, float eps, int m, int hidden, fa_bf16 *residual_out,
@@ -661,6 +738,13 @@ int execute(const Plan &plan, const fa_bf16 *const *inputs, int n, const fa_bf16
     }
     if (plan.path == FUSED_AR_PATH_TWOSTAGE && plan.chunk_rows < m)
         return run_chunks(plan, ins, n, a, m, packs, stream);
+    if (plan.path == FUSED_AR_PATH_TWOSTAGE && plan.stage1_residual) {
+        int rc = run_flat_residual(plan.step[0], ins, a.residual, total, ro, stream);
+        if (rc != FUSED_AR_OK)
+            return rc;
+        a.in[0] = ro;  // the plain RMSNorm of residual_out
+        return run_rows(plan.step[1], a, m, packs, stream);
+    }
     // Two-stage and unfused: the reduce writes the reduced rows into `out`.
     int rc = run_flat(plan.step[0], ins, total, o, stream);
     if (rc != FUSED_AR_OK)
@@ -771,21 +855,27 @@ int static_scratch(float **ptr)
 
 // The automatic path on one GPU, from a sweep of both paths over n = 2..8, hidden = 2880..32768
 // and m = 1..8192 (MI355X, graphs of calls for cache-sized problems, HBM-cold loops above): the
-// one-stage path is faster everywhere (by 6 % to 2.8x) except where a few rows are each too long
-// for one CU: with at most kTwoStageMaxM rows that each read at least kTwoStageRowBytes (the n
-// inputs and the residual), the two-stage path's flat stage 1 spreads the reads over every CU and
-// wins by 2-16 % (e.g. n = 8, hidden = 32768, m = 1: 6.5 against 7.8 us). The thresholds of the
-// pages (fused_ar_auto_path_tp) weigh the link traffic between GPUs, which one GPU does not have.
-constexpr int kTwoStageMaxM = 16;
-constexpr uint64_t kTwoStageRowBytes = 432u * 1024u;
+// one-stage path is faster everywhere (by 3 % to 2.2x) except where a few rows are each too long
+// for one CU. There the two-stage path's flat stage 1 spreads the reads over every CU: with rows
+// that read (n inputs and the residual) at least 336 KiB it wins up to 16 rows, from 432 KiB up
+// to 40 rows and from 512 KiB up to 48 rows (by up to 25 %; e.g. n = 8, hidden = 32768, m = 1:
+// 5.9 against 7.8 us). The thresholds of the pages (fused_ar_auto_path_tp) weigh the link traffic
+// between GPUs, which one GPU does not have.
+struct TwoStageTier {
+    uint64_t row_bytes;  // rows reading at least this many bytes...
+    int max_m;           // ...take the two-stage path up to this many rows
+};
+constexpr TwoStageTier kTwoStageTiers[] = {{512u * 1024u, 48}, {432u * 1024u, 40}, {336u * 1024u, 16}};
 
 extern "C" int fused_ar_auto_path(int n, int m, int hidden)
 {
     if (n < 1 || n > FUSED_AR_MAX_INPUTS || m < 0 || hidden <= 0)
         return FUSED_AR_ERR_INVALID;
     const uint64_t row_read = 2ull * (uint64_t)(n + 1) * (uint64_t)hidden;
-    return (m <= kTwoStageMaxM && row_read >= kTwoStageRowBytes) ? FUSED_AR_PATH_TWOSTAGE
-                                                                  : FUSED_AR_PATH_ONESTAGE;
+    for (const TwoStageTier &t : kTwoStageTiers)
+        if (row_read >= t.row_bytes)
+            return m <= t.max_m ? FUSED_AR_PATH_TWOSTAGE : FUSED_AR_PATH_ONESTAGE;
+    return FUSED_AR_PATH_ONESTAGE;
 }
 
 extern "C" int fused_ar_auto_path_tp(int n, int m, int hidden)

@@ -10,6 +10,7 @@
 //   k_split_reduce<N>, k_split_norm
 //                      split rows: the one-stage result with each row cut into slices on separate
 //                      workgroups, the second kernel combining the slices' square-sums.
+//   k_flat_residual<N> stage 1 with the residual add moved into it (writes residual_out).
 //   k_pipe<N, PPT>     the two-stage path in row chunks: stage 2 of one chunk and stage 1 of the
 //                      next in one launch.
 //   k_stage1_lds<N>    the LDS-staged, one-wave-per-input stage 1 that the flat reduce replaced,
@@ -316,6 +317,37 @@ __global__ void __launch_bounds__(1024) k_flat_reduce(FlatArgs a)
     // the reduced rows are read straight back by the next kernel: an ordinary store, so that they
     // can stay in the Infinity Cache
     store_pack(reinterpret_cast<char *>(a.out) + bytes, off, narrow(reduce_packs<N>(x)));
+}
+
+// Stage 1 of the two-stage path with the residual add moved into it: one thread per pack reduces
+// the N inputs, rounds to bf16, adds the residual and stores residual_out (the same per-pack
+// arithmetic as the row kernel), so that stage 2 is a plain RMSNorm of residual_out and no
+// scratch plane is written and read back. No LDS, no barrier. `out` of FlatArgs is residual_out;
+// the residual may be residual_out itself (each thread reads its pack before writing it).
+struct FlatResidualArgs {
+    FlatArgs f;
+    const u32x4 *residual;
+};
+
+template <int N, bool kStream>
+__global__ void __launch_bounds__(1024) k_flat_residual(FlatResidualArgs a)
+{
+    asm volatile("" ::"s"(a.f.in[0]), "s"(a.f.in[1]), "s"(a.f.in[2]), "s"(a.f.in[3]),
+                 "s"(a.f.in[4]), "s"(a.f.in[5]), "s"(a.f.in[6]), "s"(a.f.in[7]), "s"(a.residual),
+                 "s"(a.f.out), "s"(a.f.packs), "s"(blockDim.x));
+    const uint32_t first = blockIdx.x * blockDim.x;
+    if (first + threadIdx.x >= a.f.packs)
+        return;
+    const size_t bytes = (size_t)first * sizeof(u32x4);
+    const uint32_t off = threadIdx.x * (uint32_t)sizeof(u32x4);
+    u32x4 x[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        x[i] = load_once<kStream>(reinterpret_cast<const char *>(a.f.in[i]) + bytes, off);
+    const u32x4 res = load_once<kStream>(reinterpret_cast<const char *>(a.residual) + bytes, off);
+    __builtin_amdgcn_sched_barrier(0);  // all N + 1 loads in flight before the first add
+    // read straight back by the RMSNorm kernel: an ordinary store, so that it can stay cached
+    store_pack(reinterpret_cast<char *>(a.f.out) + bytes, off, add_residual<N>(x, res));
 }
 
 // Two-stage path in row chunks, pipelined: one launch runs stage 2 on the rows of one chunk,

@@ -52,6 +52,8 @@ def parse_args():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the unfused baseline and the design comparison")
+    ap.add_argument("--no-metric-rows", action="store_true",
+                    help="skip the metric's other rows (N=8, hidden=7168, m=2048 and 8192)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time spent timing the oracle")
     ap.add_argument("--copy-calib", action="store_true",
@@ -486,8 +488,12 @@ def path_sweep(torch, fa, ns=PATH_SWEEP_N, hiddens=PATH_SWEEP_HIDDEN, ms=PATH_SW
                 us = {}
                 for p in (1, 2):
                     us[p], how = timing_for(work, p, footprint, bytes_alg)
+                # path 2 in the pages' split (the residual added in stage 2, through the scratch)
+                us["2p"], _ = timing_for(work, 2, footprint, bytes_alg,
+                                         fa.Options(0, 0, 0, 0, 0, 0, 0, fa.RESIDUAL_STAGE2))
                 print(json.dumps({"n": n, "m": m, "hidden": hidden,
                                   "path1_us": round(us[1], 3), "path2_us": round(us[2], 3),
+                                  "path2_pages_split_us": round(us["2p"], 3),
                                   "path2_over_path1": round(us[2] / us[1], 3),
                                   "auto_path": fa.auto_path(n, m, hidden), "timing": how}),
                       flush=True)
@@ -507,7 +513,8 @@ def chunk_sweep(torch, fa):
         footprint = 2 * (n + 3) * m * hidden
         work = DeviceWorkload(torch, fa, n, m, hidden, cold_copies(footprint), seed=m + hidden)
         bytes_alg = algorithmic_bytes(n, m, hidden)
-        variants = [("path1", 1, None), ("path2", 2, None)]
+        variants = [("path1", 1, None), ("path2", 2, None),
+                    ("path2_pages_split", 2, fa.Options(0, 0, 0, 0, 0, 0, 0, fa.RESIDUAL_STAGE2))]
         for r in CHUNK_SWEEP_ROWS:
             if r < m:
                 variants += [(f"sequential_{r}", 2, fa.Options(0, 0, 0, 0, 0, r, fa.CHUNKS_SEQUENTIAL)),
@@ -649,7 +656,10 @@ def main():
     for p in (1, 2):
         if str(p) not in paths:
             paths[str(p)] = entry(p, work.time_ms(p, short, args.warmup))
-    moved_two_stage = 2 * (n + 5) * m * hidden + 2 * hidden  # + the scratch written and read back
+    # path 2 moves one plane more than the algorithmic bytes (residual_out written by stage 1 and
+    # read back by stage 2); in the pages' split two (the scratch written and read back, which the
+    # design comparison below times)
+    moved_two_stage = 2 * (n + 4) * m * hidden + 2 * hidden
     paths["2"]["moved_bytes"] = moved_two_stage
     paths["2"]["gbs_moved"] = round(moved_two_stage / (paths["2"]["us_per_call"] * 1e-6) / 1e9, 1)
     if work.ws_bytes > 0:  # the split-row form (slices chosen by the library), same problem
@@ -661,7 +671,7 @@ def main():
 
     # the other rows the metric is quoted on (N = 8, hidden = 7168, m >= 2048), path 1, HBM-cold
     metric_rows = {}
-    for mm in METRIC_ROWS_M:
+    for mm in (() if args.no_metric_rows else METRIC_ROWS_M):
         if mm == m and (n, hidden, path) == (8, 7168, 1):
             metric_rows[str(mm)] = {"us_per_call": round(ms * 1e3, 3), "gbs_algorithmic": round(gbs, 1),
                                     "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
@@ -692,6 +702,7 @@ def main():
             "twostage_flat_256": (2, fa.Options(0, fa.STAGE1_FLAT, 256, 0)),
             "twostage_flat_512": (2, fa.Options(0, fa.STAGE1_FLAT, 512, 0)),
             "twostage_lds_staged": (2, fa.Options(0, fa.STAGE1_LDS, 0, 0)),
+            "twostage_pages_split": (2, fa.Options(0, 0, 0, 0, 0, 0, 0, fa.RESIDUAL_STAGE2)),
         }
         extra["designs_us"] = {
             k: round(work.time_ms(p, short, args.warmup, o) * 1e3, 3) for k, (p, o) in designs.items()}

@@ -88,8 +88,9 @@ enum {
  *   residual_out  device [m, hidden] bf16, written. May be exactly `residual` (in place); it must
  *                 not otherwise overlap `residual`, and must not overlap an input or the weight.
  *   out           device [m, hidden] bf16, written. Must not overlap any other buffer. The
- *                 two-stage path also uses it as its scratch: stage 1 writes the reduced rows
- *                 there and stage 2 overwrites them with the normalised rows.
+ *                 two-stage path in the pages' split (see FUSED_AR_RESIDUAL_STAGE2) also uses it
+ *                 as its scratch: stage 1 writes the reduced rows there and stage 2 overwrites
+ *                 them with the normalised rows.
  *   path          FUSED_AR_PATH_AUTO, _ONESTAGE or _TWOSTAGE (aiter PR #3817, Technical Details >
  *                 1stage / 2stage); both give bit-identical residual_out.
  *   stream        HIP stream the kernels are enqueued on (0 = the null stream).
@@ -190,6 +191,23 @@ enum {
     FUSED_AR_LOAD_STREAM = 2   /* always non-temporal loads */
 };
 
+/* Where the two-stage path adds the residual (fused_ar_options.residual_stage).
+ * - STAGE2, the split of aiter PR #3817 (Technical Details > 2stage): stage 1 stores the reduced
+ *   rows (bf16) into `out` as its scratch, stage 2 reads them back, adds the residual, writes
+ *   residual_out and normalises: 2 (n + 5) m hidden bytes moved.
+ * - STAGE1: stage 1 reduces, adds the residual and writes residual_out; stage 2 is a plain
+ *   RMSNorm of residual_out: 2 (n + 4) m hidden bytes, no scratch. Bit-identical to STAGE2 (the
+ *   same roundings in the same order). On one GPU this is the faster split (by 7-10 % at the
+ *   bandwidth sizes). Across GPUs the pages keep the reduced rows in a buffer registered for
+ *   peer stores, which the caller's residual_out need not be.
+ * - AUTO: STAGE1, except with the LDS-staged stage 1 or with chunks of rows, which exist only for
+ *   STAGE2. STAGE1 together with either of those: FUSED_AR_ERR_INVALID. */
+enum {
+    FUSED_AR_RESIDUAL_AUTO = 0,
+    FUSED_AR_RESIDUAL_STAGE2 = 1,
+    FUSED_AR_RESIDUAL_STAGE1 = 2
+};
+
 /* How the two-stage path runs when it is cut into chunks of rows (fused_ar_options.stage_rows):
  * each chunk's stage 1 stores its reduced rows into `out` and its stage 2 reads them back soon
  * after, while they may still be in the L2s or the Infinity Cache, instead of after the whole
@@ -219,6 +237,8 @@ typedef struct {
                               whole call as one chunk */
     int schedule;          /* two-stage path in chunks: FUSED_AR_CHUNKS_AUTO, _SEQUENTIAL or
                               _PIPELINED */
+    int residual_stage;    /* two-stage path: where the residual is added, FUSED_AR_RESIDUAL_AUTO,
+                              _STAGE2 or _STAGE1 (see the enum above) */
 } fused_ar_options;
 
 /*
@@ -262,11 +282,12 @@ int fused_ar_reduce(const fa_bf16 *const *inputs, int n, int m, int hidden, fa_b
 
 /*
  * fused_ar_auto_path - the path FUSED_AR_PATH_AUTO takes, tuned on one MI355X where all n partial
- * sums are in local HBM: the two-stage path when m <= 16 and each row reads at least 432 KiB
- * (2 (n + 1) hidden bytes: n inputs and the residual), the one-stage path otherwise. Measured over
- * n = 2..8, hidden = 2880..32768, m = 1..8192: the one-stage path is faster everywhere except for
- * a few rows too long for one CU each (from n = 8, hidden >= 24576 or n = 6, hidden = 32768 at
- * m <= 16), where the two-stage path's flat first kernel spreads the reads over every CU.
+ * sums are in local HBM. With R = 2 (n + 1) hidden, the bytes a row reads (n inputs and the
+ * residual): the two-stage path for m <= 48 when R >= 512 KiB, for m <= 40 when R >= 432 KiB and
+ * for m <= 16 when R >= 336 KiB; the one-stage path otherwise. Measured over n = 2..8,
+ * hidden = 2880..32768, m = 1..8192: the one-stage path is faster everywhere except for a few rows
+ * too long for one CU each (from n = 8, hidden >= 20480 or n = 4, hidden = 32768 at small m),
+ * where the two-stage path's flat first kernel spreads the reads over every CU.
  * Returns 1 or 2, or FUSED_AR_ERR_INVALID for n outside [1, 8], m < 0 or hidden <= 0.
  */
 int fused_ar_auto_path(int n, int m, int hidden);
@@ -286,7 +307,8 @@ int fused_ar_auto_path_tp(int n, int m, int hidden);
 typedef struct {
     char name[32];        /* kernel name: "onestage", "stage1_reduce", "stage1_reduce_lds",
                              "stage_pipe" (stage 2 of one chunk with stage 1 of the next),
-                             "stage2_norm", "residual_add" or "rmsnorm" */
+                             "stage1_reduce_residual", "stage2_norm", "stage2_rmsnorm",
+                             "residual_add" or "rmsnorm" */
     unsigned grid;        /* workgroups per launch (the row kernels: one per row) */
     unsigned block;       /* threads per workgroup (a multiple of 64) */
     unsigned per_thread;  /* 8-element packs each thread handles per row (1 in flat kernels) */

@@ -34,8 +34,10 @@ static int cpu_checks(void)
 {
     CHECK(fused_ar_auto_path(8, 16, 7168) == FUSED_AR_PATH_ONESTAGE);
     CHECK(fused_ar_auto_path(8, 4096, 7168) == FUSED_AR_PATH_ONESTAGE);
-    CHECK(fused_ar_auto_path(8, 16, 32768) == FUSED_AR_PATH_TWOSTAGE);
-    CHECK(fused_ar_auto_path(8, 17, 32768) == FUSED_AR_PATH_ONESTAGE);
+    CHECK(fused_ar_auto_path(8, 48, 32768) == FUSED_AR_PATH_TWOSTAGE);
+    CHECK(fused_ar_auto_path(8, 49, 32768) == FUSED_AR_PATH_ONESTAGE);
+    CHECK(fused_ar_auto_path(6, 16, 24576) == FUSED_AR_PATH_TWOSTAGE);
+    CHECK(fused_ar_auto_path(6, 17, 24576) == FUSED_AR_PATH_ONESTAGE);
     CHECK(fused_ar_auto_path(0, 1, 7168) == FUSED_AR_ERR_INVALID);
     CHECK(fused_ar_auto_path(8, 1, 0) == FUSED_AR_ERR_INVALID);
     CHECK(fused_ar_auto_path_tp(8, 16, 7168) == FUSED_AR_PATH_ONESTAGE);
@@ -51,7 +53,7 @@ static int cpu_checks(void)
     CHECK(fused_ar_describe_launch(8, 4096, 7168, FUSED_AR_PATH_UNFUSED, &plan) == FUSED_AR_OK);
     CHECK(plan.kernels == 3 && strcmp(plan.launch[2].name, "rmsnorm") == 0);
     fused_ar_options opt = {FUSED_AR_WAVE_BPERMUTE, FUSED_AR_STAGE1_LDS, 0, 0, FUSED_AR_LOAD_AUTO, 0,
-                            FUSED_AR_CHUNKS_AUTO};
+                            FUSED_AR_CHUNKS_AUTO, 0};
     CHECK(fused_ar_describe_launch_ex(4, 64, 7168, FUSED_AR_PATH_TWOSTAGE, &opt, &plan) == FUSED_AR_OK);
     CHECK(strcmp(plan.launch[0].name, "stage1_reduce_lds") == 0 && plan.launch[0].block == 256);
 
@@ -78,7 +80,7 @@ static int cpu_checks(void)
     CHECK(plan.launch[0].launches == 8192u && plan.launch[0].grid == (1u << 21) &&
           plan.launch[0].block == 512u && plan.launch[0].per_thread == 1u);
     fused_ar_options lds = {FUSED_AR_WAVE_DPP, FUSED_AR_STAGE1_LDS, 0, 0, FUSED_AR_LOAD_STREAM, 0,
-                            FUSED_AR_CHUNKS_AUTO};
+                            FUSED_AR_CHUNKS_AUTO, 0};
     CHECK(fused_ar_describe_launch_ex(8, 2147483647, 32768, FUSED_AR_PATH_TWOSTAGE, &lds, &plan) ==
           FUSED_AR_OK);
     CHECK(plan.launch[0].launches == 8192u && plan.launch[0].grid == (1u << 21));
@@ -113,14 +115,22 @@ static int cpu_checks(void)
           FUSED_AR_ERR_ALIAS);
     CHECK(fused_ar_reduce(ins, 3, 2147483647, 2147483640,
                           (fa_bf16 *)(uintptr_t)0xFFFF000000000000u, NULL) == FUSED_AR_ERR_INVALID);
-    fused_ar_options bad = {0, 0, 96, 0, 0, 0, 0};
-    fused_ar_options bad_policy = {0, 0, 0, 0, 3, 0, 0};
-    fused_ar_options bad_rows = {0, 0, 0, 0, 0, (1 << 20) + 1, 0};
-    fused_ar_options bad_schedule = {0, 0, 0, 0, 0, 0, 3};
+    fused_ar_options bad = {0, 0, 96, 0, 0, 0, 0, 0};
+    fused_ar_options bad_policy = {0, 0, 0, 0, 3, 0, 0, 0};
+    fused_ar_options bad_rows = {0, 0, 0, 0, 0, (1 << 20) + 1, 0, 0};
+    fused_ar_options bad_schedule = {0, 0, 0, 0, 0, 0, 3, 0};
+    fused_ar_options bad_stage1 = {0, 0, 0, 0, 0, 0, 0, 3};
+    fused_ar_options stage1_chunks = {0, 0, 0, 0, 0, 512, 0, FUSED_AR_RESIDUAL_STAGE1};
+    CHECK(fused_ar_describe_launch_ex(8, 64, 7168, 2, &bad_stage1, &plan) == FUSED_AR_ERR_INVALID);
+    CHECK(fused_ar_describe_launch_ex(8, 64, 7168, 2, &stage1_chunks, &plan) == FUSED_AR_ERR_INVALID);
+    fused_ar_options stage1_res = {0, 0, 0, 0, 0, 0, 0, FUSED_AR_RESIDUAL_STAGE1};
+    CHECK(fused_ar_describe_launch_ex(8, 4096, 7168, 2, &stage1_res, &plan) == FUSED_AR_OK);
+    CHECK(plan.kernels == 2 && strcmp(plan.launch[0].name, "stage1_reduce_residual") == 0 &&
+          strcmp(plan.launch[1].name, "stage2_rmsnorm") == 0 && plan.launch[1].per_thread == 2u);
     CHECK(fused_ar_describe_launch_ex(8, 64, 7168, 2, &bad_rows, &plan) == FUSED_AR_ERR_INVALID);
     CHECK(fused_ar_describe_launch_ex(8, 64, 7168, 2, &bad_schedule, &plan) == FUSED_AR_ERR_INVALID);
     /* the two-stage path in chunks of one row at the largest m: no overflow in the chunk count */
-    fused_ar_options one_row = {0, 0, 0, 0, 0, 1, FUSED_AR_CHUNKS_SEQUENTIAL};
+    fused_ar_options one_row = {0, 0, 0, 0, 0, 1, FUSED_AR_CHUNKS_SEQUENTIAL, 0};
     CHECK(fused_ar_describe_launch_ex(8, 2147483647, 32768, 2, &one_row, &plan) == FUSED_AR_OK);
     CHECK(plan.kernels == 2 && plan.launch[0].launches == 2147483647u &&
           plan.launch[1].launches == 2147483647u && plan.launch[1].grid == 1u);
@@ -128,7 +138,7 @@ static int cpu_checks(void)
     CHECK(fused_ar_describe_launch_ex(8, 2147483647, 32768, 2, &one_row, &plan) == FUSED_AR_OK);
     CHECK(plan.kernels == 3 && strcmp(plan.launch[1].name, "stage_pipe") == 0 &&
           plan.launch[1].launches == 2147483646u && plan.launch[1].grid == 2u);
-    fused_ar_options big_rows = {0, 0, 0, 0, 0, 1 << 20, FUSED_AR_CHUNKS_SEQUENTIAL};
+    fused_ar_options big_rows = {0, 0, 0, 0, 0, 1 << 20, FUSED_AR_CHUNKS_SEQUENTIAL, 0};
     CHECK(fused_ar_describe_launch_ex(8, 2147483647, 32768, 2, &big_rows, &plan) == FUSED_AR_OK);
     /* 2048 chunks of 2^20 rows (the last one row short) of 2^32 packs: four flat launches each */
     CHECK(plan.launch[0].launches == 2048u * 4u && plan.launch[1].launches == 2048u);

@@ -57,7 +57,10 @@ def test_header_constants_match_binding():
                         ("FUSED_AR_LOAD_STREAM", fa.LOAD_STREAM),
                         ("FUSED_AR_CHUNKS_AUTO", fa.CHUNKS_AUTO),
                         ("FUSED_AR_CHUNKS_SEQUENTIAL", fa.CHUNKS_SEQUENTIAL),
-                        ("FUSED_AR_CHUNKS_PIPELINED", fa.CHUNKS_PIPELINED)]:
+                        ("FUSED_AR_CHUNKS_PIPELINED", fa.CHUNKS_PIPELINED),
+                        ("FUSED_AR_RESIDUAL_AUTO", fa.RESIDUAL_AUTO),
+                        ("FUSED_AR_RESIDUAL_STAGE2", fa.RESIDUAL_STAGE2),
+                        ("FUSED_AR_RESIDUAL_STAGE1", fa.RESIDUAL_STAGE1)]:
         assert re.search(rf"\b{name}\s*=\s*{value}\b", text), name
     assert re.search(rf"#define FUSED_AR_MAX_INPUTS {fa.MAX_INPUTS}\b", text)
     assert re.search(rf"#define FUSED_AR_MAX_HIDDEN {fa.MAX_HIDDEN}\b", text)
@@ -146,23 +149,29 @@ def test_reduce_checks():
 
 
 def one_gpu_path(n, m, hidden):
-    """The documented one-GPU rule: two-stage for at most 16 rows that each read at least 432 KiB
-    (n inputs and the residual), one-stage otherwise."""
-    return fa.PATH_TWOSTAGE if m <= 16 and 2 * (n + 1) * hidden >= 432 * 1024 else fa.PATH_ONESTAGE
+    """The documented one-GPU rule: with R = 2 (n + 1) hidden bytes read per row, two-stage for
+    m <= 48 when R >= 512 KiB, m <= 40 when R >= 432 KiB, m <= 16 when R >= 336 KiB; else
+    one-stage."""
+    r = 2 * (n + 1) * hidden
+    limit = 48 if r >= 512 * 1024 else 40 if r >= 432 * 1024 else 16 if r >= 336 * 1024 else -1
+    return fa.PATH_TWOSTAGE if m <= limit else fa.PATH_ONESTAGE
 
 
 def test_auto_path_rule():
     for n in range(1, 9):
-        for hidden in (8, 2880, 4096, 7168, 16384, 24568, 24576, 27648, 31592, 31600, 32768):
-            for m in (0, 1, 15, 16, 17, 32, 33, 4096):
+        for hidden in (8, 2880, 4096, 7168, 16384, 19112, 19120, 21496, 21504, 24568, 24576,
+                       27648, 28672, 29120, 29128, 32768):
+            for m in (0, 1, 15, 16, 17, 31, 32, 33, 39, 40, 41, 47, 48, 49, 4096):
                 assert fa.auto_path(n, m, hidden) == one_gpu_path(n, m, hidden), (n, m, hidden)
-    # the rule's corners: at n = 8 a row of 24576 reads exactly 432 KiB
-    assert fa.auto_path(8, 16, 24576) == fa.PATH_TWOSTAGE
-    assert fa.auto_path(8, 16, 24568) == fa.PATH_ONESTAGE
-    assert fa.auto_path(8, 17, 32768) == fa.PATH_ONESTAGE
+    # the rule's corners at n = 8: 24576 reads exactly 432 KiB, 29128 is the first width over 512
+    assert fa.auto_path(8, 40, 24576) == fa.PATH_TWOSTAGE
+    assert fa.auto_path(8, 41, 24576) == fa.PATH_ONESTAGE
+    assert fa.auto_path(8, 40, 24568) == fa.PATH_ONESTAGE
+    assert fa.auto_path(8, 16, 24568) == fa.PATH_TWOSTAGE
+    assert fa.auto_path(8, 48, 32768) == fa.PATH_TWOSTAGE
+    assert fa.auto_path(8, 49, 32768) == fa.PATH_ONESTAGE
     assert fa.auto_path(4, 1, 32768) == fa.PATH_ONESTAGE    # 320 KiB per row
-    assert fa.auto_path(6, 1, 31600) == fa.PATH_TWOSTAGE
-    assert fa.auto_path(6, 1, 31592) == fa.PATH_ONESTAGE
+    assert fa.auto_path(8, 1, 7168) == fa.PATH_ONESTAGE
     for bad in ((0, 1, 4096), (9, 1, 4096), (4, -1, 4096), (4, 1, 0), (4, 1, -8)):
         assert fa.auto_path(*bad) == fa.ERR_INVALID, bad
 
@@ -186,14 +195,14 @@ def test_launch_geometry_covers_each_row(hidden):
     for path in (1, 2):
         plan = fa.describe_launch(8, 100, hidden, path)
         rows = plan["kernels"][-1]
-        assert rows["name"] == ("onestage" if path == 1 else "stage2_norm")
+        assert rows["name"] == ("onestage" if path == 1 else "stage2_rmsnorm")
         assert rows["grid"] == 100
         assert rows["block"] % 64 == 0 and 64 <= rows["block"] <= 1024
         assert rows["block"] * rows["per_thread"] >= packs
         assert rows["block"] * rows["per_thread"] - packs < 64 * rows["per_thread"]
         if path == 2:
             flat = plan["kernels"][0]
-            assert flat["name"] == "stage1_reduce" and flat["block"] == 256
+            assert flat["name"] == "stage1_reduce_residual" and flat["block"] == 256
             assert flat["grid"] * flat["block"] * flat["per_thread"] >= 100 * packs
 
 
@@ -226,8 +235,8 @@ def test_launch_geometry_by_row_count():
 
 def test_launch_geometry_auto_and_empty():
     assert fa.describe_launch(8, 17, 7168)["path"] == 1
-    assert fa.describe_launch(8, 16, 32768)["path"] == 2
-    assert fa.describe_launch(8, 17, 32768)["path"] == 1
+    assert fa.describe_launch(8, 48, 32768)["path"] == 2
+    assert fa.describe_launch(8, 49, 32768)["path"] == 1
     assert fa.describe_launch(4, 0, 7168, 1)["kernels"] == []
     with pytest.raises(fa.FusedArError):
         fa.describe_launch(4, 8, 12, 1)
@@ -269,7 +278,10 @@ def test_options_struct_matches_header():
     fa.Options(0, 0, 32, 0), fa.Options(0, 0, 100, 0), fa.Options(0, 0, 2048, 0),
     fa.Options(0, 0, 0, 3), fa.Options(0, 0, 0, 8), fa.Options(0, 0, 0, 0, 3),
     fa.Options(0, 0, 0, 0, -1), fa.Options(0, 0, 0, 0, 0, -2), fa.Options(0, 0, 0, 0, 0, (1 << 20) + 1),
-    fa.Options(0, 0, 0, 0, 0, 0, 3), fa.Options(0, 0, 0, 0, 0, 0, -1)])
+    fa.Options(0, 0, 0, 0, 0, 0, 3), fa.Options(0, 0, 0, 0, 0, 0, -1),
+    fa.Options(0, 0, 0, 0, 0, 0, 0, 3), fa.Options(0, 0, 0, 0, 0, 0, 0, -1),
+    fa.Options(0, fa.STAGE1_LDS, 0, 0, 0, 0, 0, fa.RESIDUAL_STAGE1),
+    fa.Options(0, 0, 0, 0, 0, 512, 0, fa.RESIDUAL_STAGE1)])
 def test_bad_options_rejected_before_launch(opts):
     ins = [addr(i) for i in range(4)]
     rc = fa.fused_ar_rmsnorm_ex_ptrs(ins, addr(10), addr(11), 1e-6, 8, 4096, addr(12), addr(13),
@@ -314,11 +326,40 @@ def test_chunked_two_stage_plans():
                                           ("stage2_norm", 1096, 448, 2, 1)]
     # chunks of 2^20 packs and more take the larger flat workgroup
     assert plan(8192, 1024, seq, n=8, hidden=8192)[0] == ("stage1_reduce", 2048, 512, 1, 8)
-    # one chunk (rows >= m, or -1) is the plain two-stage plan; path 1 ignores the options
+    # one chunk (rows >= m) is the plain two-stage plan in the pages' split (chunks exist only in
+    # it; -1 asks for one chunk and leaves the split to the library); path 1 ignores the options
+    pages = [(k["name"], k["grid"], k["block"], k["per_thread"], k["launches"])
+             for k in fa.describe_launch(4, 4096, 7168, 2,
+                                         fa.Options(0, 0, 0, 0, 0, 0, 0, fa.RESIDUAL_STAGE2))["kernels"]]
+    assert plan(4096, 4096, pipe) == pages
+    assert [k[0] for k in pages] == ["stage1_reduce", "stage2_norm"]
+    assert [k[0] for k in plan(4096, -1, seq)] == ["stage1_reduce_residual", "stage2_rmsnorm"]
     whole = plan(4096, 0, 0)
-    assert plan(4096, 4096, pipe) == whole and plan(4096, -1, seq) == whole
-    assert [k[0] for k in whole] == ["stage1_reduce", "stage2_norm"]
     assert plan(4096, 512, pipe, path=1) == plan(4096, 0, 0, path=1)
+
+
+def test_residual_stage_plans():
+    """Where the two-stage path adds the residual: by default (and asked) in stage 1, a flat
+    reduce + residual kernel over all packs then the plain RMSNorm row kernel; in the pages' split
+    a flat reduce into the scratch then the row kernel that adds the residual; the same grids and
+    geometry either way. The LDS-staged stage 1 and chunks of rows take the pages' split; other
+    paths ignore the option."""
+    stage1 = fa.Options(0, 0, 0, 0, 0, 0, 0, fa.RESIDUAL_STAGE1)
+    pages = fa.Options(0, 0, 0, 0, 0, 0, 0, fa.RESIDUAL_STAGE2)
+    k = fa.describe_launch(8, 4096, 7168, 2, stage1)["kernels"]
+    assert [x["name"] for x in k] == ["stage1_reduce_residual", "stage2_rmsnorm"]
+    assert fa.describe_launch(8, 4096, 7168, 2)["kernels"] == k
+    assert [x["name"] for x in fa.describe_launch(8, 4096, 7168, 2, fa.Options(0, fa.STAGE1_LDS, 0, 0))["kernels"]] == \
+        ["stage1_reduce_lds", "stage2_norm"]
+    whole = fa.describe_launch(8, 4096, 7168, 2, pages)["kernels"]
+    assert [x["name"] for x in whole] == ["stage1_reduce", "stage2_norm"]
+    for a, b in zip(k, whole):
+        assert (a["grid"], a["block"], a["per_thread"], a["launches"], a["lds_bytes"]) == \
+            (b["grid"], b["block"], b["per_thread"], b["launches"], b["lds_bytes"])
+    for opt in (stage1, pages):
+        assert fa.describe_launch(8, 4096, 7168, 1, opt) == fa.describe_launch(8, 4096, 7168, 1)
+        assert fa.describe_launch(4, 100, 2880, fa.PATH_UNFUSED, opt) == \
+            fa.describe_launch(4, 100, 2880, fa.PATH_UNFUSED)
 
 
 def test_unfused_plan_and_checks():

@@ -159,8 +159,11 @@ def check_plan(n, m, packs, path, wave, stage1, block, ppt, policy, rows=0, sche
         assert e.value.status == fa.ERR_SHAPE
         return
     plan = fa.describe_launch(n, m, hidden, path, opt)
-    # automatic: two-stage for at most 16 rows that each read at least 432 KiB, else one-stage
-    want_path = path if path else (2 if m <= 16 and 2 * (n + 1) * hidden >= 432 * 1024 else 1)
+    # automatic: two-stage for a few rows that each read a lot (R = 2 (n + 1) hidden bytes): up
+    # to 48 rows from R = 512 KiB, 40 from 432 KiB, 16 from 336 KiB; else one-stage
+    r = 2 * (n + 1) * hidden
+    limit = 48 if r >= 512 * 1024 else 40 if r >= 432 * 1024 else 16 if r >= 336 * 1024 else -1
+    want_path = path if path else (2 if m <= limit else 1)
     assert plan["path"] == want_path
     if m == 0:
         assert plan["kernels"] == []
@@ -172,9 +175,13 @@ def check_plan(n, m, packs, path, wave, stage1, block, ppt, policy, rows=0, sche
         check_chunked_plan(ks, n, m, packs, stage1, block, rows=chunk, pipelined=sched == 2,
                            geometry=rows_geometry, stream=stream, capped=capped, s1=s1)
         return
+    # two-stage: the residual add in stage 1 unless the LDS-staged stage 1 or chunks ask for the
+    # pages' split (stage 1 into the scratch, stage 2 adds the residual)
+    in_stage1 = not stage1 and rows <= 0
+    two = ["stage1_reduce_residual", "stage2_rmsnorm"] if in_stage1 else [s1, "stage2_norm"]
     assert [k["name"] for k in ks] == {
         1: ["onestage"],
-        2: [s1, "stage2_norm"],
+        2: two,
         3: [s1, "residual_add", "rmsnorm"]}[want_path]
     # the row kernel: one workgroup per row, whole waves, every pack of a row covered once
     k_rows = ks[-1]

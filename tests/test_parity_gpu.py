@@ -129,8 +129,8 @@ def test_paths_agree_bit_for_bit():
 def test_auto_path_matches_explicit():
     """The automatic path gives the bits of the path the rule names, on either side of the rule's
     corners (two-stage only for a few rows of wide, many-input rows), and the oracle's result."""
-    for n, m, hidden in [(8, 16, 2880), (4, 33, 2880), (8, 16, 32768), (8, 17, 32768),
-                         (6, 3, 32768), (4, 3, 32768)]:
+    for n, m, hidden in [(8, 16, 2880), (4, 33, 2880), (8, 48, 32768), (8, 49, 32768),
+                         (6, 16, 24576), (6, 17, 24576), (4, 3, 32768)]:
         p = synth.make_problem(n, m, hidden, seed=8)
         announce(f"auto n={n} m={m} hidden={hidden} -> path {fa.auto_path(n, m, hidden)}")
         r0 = run_gpu(p, 0)
@@ -138,8 +138,8 @@ def test_auto_path_matches_explicit():
         assert np.array_equal(r0[0], r[0]) and np.array_equal(r0[1], r[1])
         want_ro, want_out = oracle_rows(p)
         assert_parity(f"auto n={n} m={m} hidden={hidden}", r0[0], r0[1], want_ro, want_out)
-    assert fa.auto_path(8, 16, 32768) == fa.PATH_TWOSTAGE
-    assert fa.auto_path(8, 17, 32768) == fa.PATH_ONESTAGE
+    assert fa.auto_path(8, 48, 32768) == fa.PATH_TWOSTAGE
+    assert fa.auto_path(8, 49, 32768) == fa.PATH_ONESTAGE
 
 
 # ------------------------------------------------------------------------- the reduce alone
@@ -539,12 +539,17 @@ OPTION_SETS = [
     (fa.WAVE_DPP, fa.STAGE1_FLAT, 0, 0, 0, 7, fa.CHUNKS_PIPELINED),
     (fa.WAVE_BPERMUTE, fa.STAGE1_LDS, 0, 0, fa.LOAD_STREAM, 2, fa.CHUNKS_SEQUENTIAL),
     (fa.WAVE_DPP, fa.STAGE1_FLAT, 256, 0, fa.LOAD_STREAM, 1, fa.CHUNKS_PIPELINED),
+    # where the two-stage path adds the residual: the pages' split (stage 2, through the scratch)
+    # or stage 1 (the default)
+    (fa.WAVE_DPP, fa.STAGE1_FLAT, 0, 0, 0, 0, 0, fa.RESIDUAL_STAGE2),
+    (fa.WAVE_BPERMUTE, fa.STAGE1_FLAT, 512, 0, fa.LOAD_STREAM, 0, 0, fa.RESIDUAL_STAGE2),
+    (fa.WAVE_DPP, fa.STAGE1_FLAT, 256, 0, fa.LOAD_CACHED, -1, 0, fa.RESIDUAL_STAGE1),
 ]
 
 
 def _option_id(o):
-    o = tuple(o) + (0,) * (7 - len(o))
-    return "w{}-s{}-b{}-p{}-l{}-r{}-c{}".format(*o)
+    o = tuple(o) + (0,) * (8 - len(o))
+    return "w{}-s{}-b{}-p{}-l{}-r{}-c{}-x{}".format(*o)
 
 
 @pytest.mark.parametrize("opt", OPTION_SETS, ids=_option_id)
@@ -567,22 +572,33 @@ def test_design_options_are_bit_identical(opt, n, m, hidden):
     assert_parity("options", host(ro_o), host(out_o), want_ro, want_out)
 
 
-@pytest.mark.parametrize("schedule", [fa.CHUNKS_SEQUENTIAL, fa.CHUNKS_PIPELINED])
-def test_chunked_two_stage_on_a_long_streaming_call(schedule):
-    """The two-stage path in chunks of 512 rows on a call that streams and caps its row
-    workgroups (two packs per thread): the oracle's result, and path 1's bits."""
+@pytest.mark.parametrize("variant", ["sequential", "pipelined", "residual in stage 1",
+                                     "pages' split"])
+def test_two_stage_variants_on_a_long_streaming_call(variant):
+    """The two-stage path in chunks of 512 rows, with the residual add in stage 1 (the default) or
+    in stage 2 (the pages' split), on a call that streams and caps its row workgroups (two packs
+    per thread), also in place: the oracle's result, and path 1's bits."""
+    opts = {"sequential": fa.Options(0, 0, 0, 0, 0, 512, fa.CHUNKS_SEQUENTIAL),
+            "pipelined": fa.Options(0, 0, 0, 0, 0, 512, fa.CHUNKS_PIPELINED),
+            "residual in stage 1": fa.Options(0, 0, 0, 0, 0, 0, 0, fa.RESIDUAL_STAGE1),
+            "pages' split": fa.Options(0, 0, 0, 0, 0, 0, 0, fa.RESIDUAL_STAGE2)}
     p = synth.make_problem(4, 2100, 7168, seed=23, name="chunks")
     ins = [dev(x) for x in p.inputs]
     res, w = dev(p.residual), dev(p.weight)
-    announce(f"chunked two-stage schedule={schedule} n=4 m=2100 hidden=7168")
+    announce(f"two-stage {variant} n=4 m=2100 hidden=7168")
     ro1, out1 = fa.fused_ar_rmsnorm(ins, res, w, p.eps, path=1)
-    ro, out = fa.fused_ar_rmsnorm(ins, res, w, p.eps, path=2,
-                                  options=fa.Options(0, 0, 0, 0, 0, 512, schedule))
+    ro, out = fa.fused_ar_rmsnorm(ins, res, w, p.eps, path=2, options=opts[variant])
     torch.cuda.synchronize()
     assert torch.equal(ro.view(torch.int16), ro1.view(torch.int16))
     assert torch.equal(out.view(torch.int16), out1.view(torch.int16))
     want_ro, want_out = oracle_rows(p)
-    assert_parity("chunks", host(ro), host(out), want_ro, want_out)
+    assert_parity(variant, host(ro), host(out), want_ro, want_out)
+    # in place: residual_out is the residual's own buffer
+    res_in_place = res.clone()
+    ro, out = fa.fused_ar_rmsnorm(ins, res_in_place, w, p.eps, residual_out=res_in_place, path=2,
+                                  options=opts[variant])
+    torch.cuda.synchronize()
+    assert_parity(f"{variant} in place", host(ro), host(out), want_ro, want_out)
 
 
 @pytest.mark.parametrize("ppt", [1, 2, 4])
@@ -620,12 +636,16 @@ def test_randomized_shapes_paths_and_options():
         opt = fa.Options(int(rng.integers(0, 2)), int(rng.integers(0, 2)),
                          int(rng.choice([0, 64, 256, 512, 1024])), ppt, int(rng.integers(0, 3)),
                          int(rng.choice([0, 0, 1, 13, 64])), int(rng.integers(0, 3)))
+        opt.residual_stage = int(rng.integers(0, 3))
+        if opt.residual_stage == fa.RESIDUAL_STAGE1 and (opt.stage1 == fa.STAGE1_LDS
+                                                          or opt.stage_rows > 0):
+            opt.residual_stage = fa.RESIDUAL_AUTO  # stage 1 has no LDS-staged or chunked form
         eps = float(rng.choice([1e-6, 1e-5, 0.1]))
         dist = "stress" if rng.random() < 0.3 else "normal"
         p = synth.make_problem(n, m, hidden, seed=5000 + case, eps=eps, dist=dist, name="random")
         name = (f"random case {case}: n={n} m={m} hidden={hidden} path={path} "
                 f"options=({opt.wave_reduce},{opt.stage1},{opt.stage1_block},{opt.packs_per_thread},"
-                f"{opt.load_policy},{opt.stage_rows},{opt.schedule}) "
+                f"{opt.load_policy},{opt.stage_rows},{opt.schedule},{opt.residual_stage}) "
                 f"eps={eps} {dist}")
         announce(name)
         ins = [dev(x) for x in p.inputs]
