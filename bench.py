@@ -375,6 +375,22 @@ def time_oracle(oracle, prob, eps, bytes_alg):
             "threads_match_single": same}
 
 
+def design_options(fa):
+    """The designs compared in the bench line (name -> (path, options)): the one-stage wave sum by
+    DPP (the default) or by ds_bpermute; the two-stage path in the pages' split (stage 2 adds the
+    residual) with the flat stage 1 in workgroups of 256 or 512 threads or the LDS-staged stage 1;
+    and the library's two-stage default, the residual added in stage 1."""
+    pages = fa.RESIDUAL_STAGE2
+    return {
+        "onestage_dpp": (1, None),
+        "onestage_bpermute": (1, fa.Options(fa.WAVE_BPERMUTE, 0, 0, 0)),
+        "twostage_flat_256": (2, fa.Options(0, fa.STAGE1_FLAT, 256, 0, 0, 0, 0, pages)),
+        "twostage_flat_512": (2, fa.Options(0, fa.STAGE1_FLAT, 512, 0, 0, 0, 0, pages)),
+        "twostage_lds_staged": (2, fa.Options(0, fa.STAGE1_LDS, 0, 0, 0, 0, 0, pages)),
+        "twostage_residual_in_stage1": (2, None),
+    }
+
+
 def per_rank_share(torch, fa, work, steps, warmup):
     """One rank's share of the two-stage path in an N-way tensor-parallel group, on local HBM:
     stage 1 reduces only this rank's 1/N slice of the packs (here the first m/N rows), stage 2
@@ -696,16 +712,9 @@ def main():
                                  moved_bytes=moved_unfused,
                                  gbs_moved=round(moved_unfused / (ums * 1e-3) / 1e9, 1),
                                  fused_speedup=round(ums / ms, 3))}
-        designs = {
-            "onestage_dpp": (1, None),
-            "onestage_bpermute": (1, fa.Options(fa.WAVE_BPERMUTE, 0, 0, 0)),
-            "twostage_flat_256": (2, fa.Options(0, fa.STAGE1_FLAT, 256, 0)),
-            "twostage_flat_512": (2, fa.Options(0, fa.STAGE1_FLAT, 512, 0)),
-            "twostage_lds_staged": (2, fa.Options(0, fa.STAGE1_LDS, 0, 0)),
-            "twostage_pages_split": (2, fa.Options(0, 0, 0, 0, 0, 0, 0, fa.RESIDUAL_STAGE2)),
-        }
         extra["designs_us"] = {
-            k: round(work.time_ms(p, short, args.warmup, o) * 1e3, 3) for k, (p, o) in designs.items()}
+            k: round(work.time_ms(p, short, args.warmup, o) * 1e3, 3)
+            for k, (p, o) in design_options(fa).items()}
         extra["per_rank_share"] = per_rank_share(torch, fa, work, short, args.warmup)
         extra["per_rank_share"]["onestage_us"] = round(ms * 1e3, 3)
 
@@ -720,17 +729,10 @@ def main():
             decode[str(dm)] = round(dw.graph_latency_us(1), 3)
             if not args.no_extra and dm in (1, 32):
                 decode_designs[str(dm)] = {
-                    "onestage_dpp": decode[str(dm)],
-                    "onestage_bpermute": round(dw.graph_latency_us(
-                        1, fa.Options(fa.WAVE_BPERMUTE, 0, 0, 0)), 3),
-                    "twostage_flat_256": round(dw.graph_latency_us(
-                        2, fa.Options(0, fa.STAGE1_FLAT, 256, 0)), 3),
-                    "twostage_flat_512": round(dw.graph_latency_us(
-                        2, fa.Options(0, fa.STAGE1_FLAT, 512, 0)), 3),
-                    "twostage_lds_staged": round(dw.graph_latency_us(
-                        2, fa.Options(0, fa.STAGE1_LDS, 0, 0)), 3),
-                    "unfused": round(dw.graph_latency_us(fa.PATH_UNFUSED), 3),
-                }
+                    k: (decode[str(dm)] if k == "onestage_dpp" else
+                        round(dw.graph_latency_us(p, o), 3))
+                    for k, (p, o) in design_options(fa).items()}
+                decode_designs[str(dm)]["unfused"] = round(dw.graph_latency_us(fa.PATH_UNFUSED), 3)
             del dw
         if args.no_extra:
             decode_designs = None
