@@ -20,6 +20,7 @@ import ctypes
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -80,6 +81,10 @@ def parse_args():
     ap.add_argument("--chunk-sweep", action="store_true",
                     help="only time the two-stage path whole and in row chunks (sequential and "
                          "pipelined) on the HBM-cold shapes: one JSON line per shape")
+    ap.add_argument("--load-sources", action="store_true",
+                    help="only time path 1 with ordinary, non-temporal and automatic loads on "
+                         "inputs just written by another kernel, just read by the call before, or "
+                         "evicted: one JSON line per shape")
     return ap.parse_args()
 
 
@@ -547,6 +552,57 @@ def chunk_sweep(torch, fa):
         torch.cuda.empty_cache()
 
 
+LOAD_SOURCE_SHAPES = ((8, 128, 7168), (8, 256, 7168), (8, 512, 7168), (8, 1024, 7168),
+                      (4, 512, 7168), (4, 1024, 7168), (8, 1024, 2880), (8, 2048, 2880),
+                      (8, 4096, 7168))
+
+
+def load_sources(torch, fa):
+    """Path 1 with each load policy on inputs from three sources, one buffer set per shape:
+    `written` - every input plane and the residual filled by another kernel just before the call
+    (a producer writing the partial sums); `read` - the same inputs read by the call before;
+    `evicted` - 768 MiB written elsewhere just before (the inputs pushed out of the caches, which
+    hold another kernel's writes instead). Each call is timed alone by events around it: median of
+    25 calls, best of two rounds, us."""
+    sink = torch.empty(768 << 20, dtype=torch.uint8, device="cuda")
+    policies = (("cached", fa.Options(0, 0, 0, 0, fa.LOAD_CACHED, 0, 0, 0)),
+                ("stream", fa.Options(0, 0, 0, 0, fa.LOAD_STREAM, 0, 0, 0)), ("auto", None))
+    for n, m, hidden in LOAD_SOURCE_SHAPES:
+        work = DeviceWorkload(torch, fa, n, m, hidden, 1, seed=m + hidden)
+        planes = work.sets[0]["keep"]  # the n inputs and the residual
+
+        def written():
+            for t in planes:
+                t.fill_(0.5)
+
+        sources = (("written", written), ("read", lambda: work.call(0, 1)),
+                   ("evicted", lambda: sink.fill_(1)))
+        stream = torch.cuda.current_stream()
+        best = {}
+        for _ in range(2):
+            for pname, o in policies:
+                for sname, before in sources:
+                    times = []
+                    for _ in range(25):
+                        before()
+                        start = torch.cuda.Event(enable_timing=True)
+                        end = torch.cuda.Event(enable_timing=True)
+                        start.record(stream)
+                        work.call(0, 1, o)
+                        end.record(stream)
+                        torch.cuda.synchronize()
+                        times.append(start.elapsed_time(end) * 1e3)
+                    key = f"{sname}_{pname}"
+                    best[key] = min(best.get(key, float("inf")), statistics.median(times))
+        print(json.dumps({"n": n, "m": m, "hidden": hidden,
+                          "read_mib": round(2 * (n + 1) * m * hidden / 2**20, 1),
+                          "auto_streams": bool(fa.describe_launch(n, m, hidden, 1)["kernels"][0]["streaming"]),
+                          "us": {k: round(v, 2) for k, v in best.items()}}), flush=True)
+        del work, planes
+        torch.cuda.empty_cache()
+    del sink
+
+
 class DeviceWorkload(Workload):
     """A Workload whose buffers are filled on the GPU (seeded normal values), for shapes too large
     to generate on the host; the timing does not depend on the values."""
@@ -633,6 +689,9 @@ def main():
         return
     if args.chunk_sweep:
         chunk_sweep(torch, fa)
+        return
+    if args.load_sources:
+        load_sources(torch, fa)
         return
     if args.ceilings:
         hbm_ceilings(torch)

@@ -74,3 +74,15 @@ def test_cold_copies_exceed_the_cache():
     for fp in (200 << 20, 646 << 20, 1 << 30, 3 << 30):
         c = bench.cold_copies(fp)
         assert c * fp >= (1 << 30) or c == 8
+
+
+def test_load_source_shapes_straddle_the_stream_rule():
+    # the shapes that compare load policies: every one but the largest reads at most 128 MiB and so
+    # takes ordinary loads automatically; the plan says so without touching a GPU
+    import all_reduce_residual_way_amd as fa
+    streams = {}
+    for n, m, hidden in bench.LOAD_SOURCE_SHAPES:
+        read = 2 * (n + 1) * m * hidden
+        streams[(n, m, hidden)] = bool(fa.describe_launch(n, m, hidden, 1)["kernels"][0]["streaming"])
+        assert streams[(n, m, hidden)] == (read > (128 << 20))
+    assert sum(streams.values()) == 1 and streams[(8, 4096, 7168)]
