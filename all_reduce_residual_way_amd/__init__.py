@@ -299,6 +299,13 @@ def _stream_handle(stream, device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _check_stream(stream, device):
+    """Raise unless ``stream`` (a torch.cuda.Stream, or None for the current stream) belongs to
+    ``device``, the device of the tensors: the kernels run on the device the stream belongs to."""
+    if stream is not None and stream.device != device:
+        raise ValueError(f"stream is on {stream.device}, the tensors on {device}")
+
+
 def _on_stream(t, stream):
     """A tensor allocated here for work enqueued on ``stream`` (not the current stream): recorded
     on that stream, so that torch's caching allocator does not hand its memory out again before
@@ -317,6 +324,7 @@ def _prepare(inputs, residual, weight, residual_out, out, stream=None):
     shape = residual.shape
     m, hidden = shape
     device = residual.device
+    _check_stream(stream, device)
     index = device.index if device.type == "cuda" else -2  # get_device() is -1 on the CPU
     if not (all(_fits(x, shape, index, torch) for x in inputs)
             and _fits(residual, shape, index, torch) and _fits(weight, (hidden,), index, torch)):
@@ -399,6 +407,7 @@ def fused_ar_reduce(inputs, *, reduced=None, stream=None):
     m, hidden = x0.shape
     for i, x in enumerate(inputs):
         _check_tensor(x, f"inputs[{i}]", (m, hidden), x0.device)
+    _check_stream(stream, x0.device)
     if reduced is None:
         reduced = _on_stream(torch.empty_like(x0), stream)
     _check_tensor(reduced, "reduced", (m, hidden), x0.device)

@@ -265,6 +265,19 @@ def test_binding_rejects_bad_tensors_without_a_gpu():
         fa.fused_ar_reduce([x])
 
 
+def test_stream_of_another_device_rejected():
+    # the kernels run on the stream's device, so a stream of another device than the tensors' is
+    # refused before anything is enqueued (checked here with stand-ins: no GPU is needed)
+    import types
+
+    import torch
+    cuda0, cuda1 = torch.device("cuda", 0), torch.device("cuda", 1)
+    fa._check_stream(None, cuda0)
+    fa._check_stream(types.SimpleNamespace(device=torch.device("cuda:0")), cuda0)
+    with pytest.raises(ValueError, match="stream is on cuda:1"):
+        fa._check_stream(types.SimpleNamespace(device=cuda1), cuda0)
+
+
 def test_options_struct_matches_header():
     with open(HEADER) as f:
         text = f.read()
