@@ -156,7 +156,9 @@ size_t fused_ar_split_workspace_bytes(int m, int hidden, int splits);
  * that forbid hipMalloc. The slice square-sums go to a fixed device array of the library,
  * FUSED_AR_STATIC_SCRATCH_FLOATS floats, of which each GPU the library runs on holds its own copy
  * until the process ends; the call itself allocates nothing (no hipMalloc, no hipFree). The first
- * call on a device looks up that device's copy (hipGetSymbolAddress, with the device current).
+ * call on a device looks up that device's copy (hipGetSymbolAddress, with the device current);
+ * callers that will capture it make one call on that device before capturing (tested: captured
+ * calls replayed with eager calls of other shapes in between give the eager result).
  *   Limit: m * slices <= FUSED_AR_STATIC_SCRATCH_FLOATS (slices as fused_ar_split_workspace_bytes
  *   counts them: m <= 16384 at hidden 7168, m <= 4096 at hidden 32768, with the default slices);
  *   larger calls return FUSED_AR_ERR_SCRATCH and launch nothing.

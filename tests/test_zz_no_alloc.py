@@ -81,3 +81,47 @@ def test_static_scratch_rejects_calls_beyond_it():
     assert rc == fa.ERR_SCRATCH
     torch.cuda.synchronize()
     assert not ro.view(torch.int16).any() and not out.view(torch.int16).any()  # nothing launched
+
+
+def test_static_scratch_under_graph_replay():
+    """Calls of the static-scratch form captured in a HIP graph give the oracle's result on every
+    replay, with an eager call of another shape between replays: that call overwrites the shared
+    scratch, and each captured call rewrites every slot it reads before reading it."""
+    lib = fa.library()
+
+    def device_problem(p):
+        ins = [dev(x) for x in p.inputs]
+        res, w = dev(p.residual), dev(p.weight)
+        return dict(ins=ins, arr=(VP * p.n)(*[x.data_ptr() for x in ins]), res=res, w=w,
+                    ro=torch.empty_like(res), out=torch.empty_like(res))
+
+    def call(p, d, stream):
+        return lib.fused_ar_rmsnorm_split_static(d["arr"], p.n, d["res"].data_ptr(),
+                                                 d["w"].data_ptr(), p.eps, p.m, p.hidden,
+                                                 d["ro"].data_ptr(), d["out"].data_ptr(), 0, stream)
+
+    p = synth.make_problem(8, 4, 7168, seed=35, name="static scratch in a graph")
+    q = synth.make_problem(2, 300, 16384, seed=36, name="static scratch between replays")
+    dp, dq = device_problem(p), device_problem(q)
+    want_p = oracle.fused(p.inputs, p.residual, p.weight, p.eps)
+    want_q = oracle.fused(q.inputs, q.residual, q.weight, q.eps)
+    print("[gpu case] static-scratch split rows: eager call before capture", flush=True)
+    assert call(q, dq, torch.cuda.current_stream().cuda_stream) == fa.OK
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        capture = torch.cuda.current_stream().cuda_stream
+        for _ in range(10):
+            assert call(p, dp, capture) == fa.OK
+    for replay in range(3):
+        print(f"[gpu case] static-scratch split rows: graph replay {replay}", flush=True)
+        dp["ro"].zero_()
+        dp["out"].zero_()
+        dq["out"].zero_()
+        assert call(q, dq, torch.cuda.current_stream().cuda_stream) == fa.OK
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for (want_ro, want_out), d in ((want_p, dp), (want_q, dq)):
+            assert np.array_equal(host(d["ro"]), want_ro), replay
+            assert ulp_diff(host(d["out"]), want_out).max() <= 1, replay
