@@ -211,23 +211,6 @@ constexpr unsigned kRowCapLds = 64u * 1024u;
 
 bool rows_capped(bool stream, int m) { return stream && m > kTwoPackMaxM; }
 
-// residual_out by ordinary instead of non-temporal stores in the row kernel: on capped calls (two
-// or four packs per thread, N >= 2) whose residual_out plane exceeds the L2s' 32 MiB. Measured on
-// MI355X side by side, HBM-cold, % of peak: +0.5 at N = 8, m = 4096, hidden 7168, +1.4 at
-// m = 8192, +1.2 at 8192 x 8192, +1.0 at N = 4, m = 4096, +1.9 at hidden 16384, m = 4096, +2.6 at
-// N = 4, hidden 4096, m = 8192; but -0.75 at N = 8, m = 2048 (a 29 MB plane), -0.6 to -1.3 on
-// uncapped streamed calls (m <= 1024), -1.4 for the single-input row kernel of the pages' split
-// (N = 1), neutral with one pack per thread; cache-resident calls lose by it (up to 11 %). Dirty
-// lines left in the L2s are written back when a kernel ends, a cost that only large planes
-// amortise.
-constexpr uint64_t kPlainResidualOutMinBytes = uint64_t(32) << 20;
-
-bool plain_residual_out(bool capped, int n, int ppt, int m, int hidden)
-{
-    return capped && n >= 2 && (ppt == 2 || ppt == 4) &&
-           2ull * (uint64_t)m * (uint64_t)hidden > kPlainResidualOutMinBytes;
-}
-
 int row_geometry(int packs, int m, int forced_ppt, bool capped, int *ppt, int *threads)
 {
     int k = forced_ppt;
@@ -276,39 +259,8 @@ const void *row_kernel_bs(int n, int ppt, bool residual)
     }
 }
 
-// The one-stage kernel with ordinary residual_out stores (plain_residual_out): n >= 2, streamed,
-// two or four packs per thread.
-template <int N, bool kB>
-const void *plain_residual_out_np(int ppt)
+const void *row_kernel(int n, int ppt, bool bpermute, bool residual, bool stream)
 {
-    switch (ppt) {
-    case 2: return reinterpret_cast<const void *>(&fa::k_rows<N, 2, kB, true, true, true>);
-    case 4: return reinterpret_cast<const void *>(&fa::k_rows<N, 4, kB, true, true, true>);
-    default: return nullptr;
-    }
-}
-
-template <bool kB>
-const void *plain_residual_out_kernel(int n, int ppt)
-{
-    switch (n) {
-    case 2: return plain_residual_out_np<2, kB>(ppt);
-    case 3: return plain_residual_out_np<3, kB>(ppt);
-    case 4: return plain_residual_out_np<4, kB>(ppt);
-    case 5: return plain_residual_out_np<5, kB>(ppt);
-    case 6: return plain_residual_out_np<6, kB>(ppt);
-    case 7: return plain_residual_out_np<7, kB>(ppt);
-    case 8: return plain_residual_out_np<8, kB>(ppt);
-    default: return nullptr;
-    }
-}
-
-const void *row_kernel(int n, int ppt, bool bpermute, bool residual, bool stream,
-                       bool plain_ro = false)
-{
-    if (plain_ro)
-        return bpermute ? plain_residual_out_kernel<true>(n, ppt)
-                        : plain_residual_out_kernel<false>(n, ppt);
     if (bpermute)
         return stream ? row_kernel_bs<true, true>(n, ppt, residual)
                       : row_kernel_bs<true, false>(n, ppt, residual);
@@ -535,8 +487,7 @@ int make_plan(int n, int m, int hidden, int path, const Options &o, Plan *plan)
     if (capped)
         rows.lds = kRowCapLds;
     if (path == FUSED_AR_PATH_ONESTAGE) {
-        rows.kernel = row_kernel(n, ppt, o.bpermute, true, stream,
-                                 plain_residual_out(capped, n, ppt, m, hidden));
+        rows.kernel = row_kernel(n, ppt, o.bpermute, true, stream);
         rows.name = "onestage";
         plan->steps = 1;
         plan->step[0] = rows;

@@ -192,15 +192,11 @@ __device__ __forceinline__ u32x4 load_once(const char *base, uint32_t off)
 //   kStream    non-temporal loads of the inputs and the residual (see load_once); with N == 1 the
 //              input is the reduced rows the flat reduce has just stored (two-stage path, unfused
 //              sequence), which may still be in the Infinity Cache, so it is always loaded normally.
-//   kPlainResidualOut  residual_out by ordinary instead of non-temporal stores: the variant the
-//              host picks for long streamed calls (plain_residual_out in fused_ar.hip).
-template <int N, int PPT, bool kBpermute, bool kResidual, bool kStream,
-          bool kPlainResidualOut = false>
+template <int N, int PPT, bool kBpermute, bool kResidual, bool kStream>
 __device__ __forceinline__ void row_pass(const RowArgs &a, float eps, float inv_hidden,
                                          int tiny_eps, uint32_t row, float *slots)
 {
     static_assert(kResidual || N == 1, "the plain RMSNorm reads one input");
-    static_assert(!kPlainResidualOut || (kResidual && kStream), "a streamed call's residual_out");
     const uint32_t tid = threadIdx.x;
     const uint32_t nthreads = blockDim.x;
     const uint32_t packs = (uint32_t)a.packs;
@@ -237,10 +233,7 @@ __device__ __forceinline__ void row_pass(const RowArgs &a, float eps, float inv_
                 F8 sum = widen(narrow(reduce_packs<N>(x)));  // the reduced value, in bf16
                 add_into(sum, widen(res));
                 ro[k] = narrow(sum);
-                if constexpr (kPlainResidualOut)
-                    store_pack(residual_out, off, ro[k]);
-                else
-                    store_stream(residual_out, off, ro[k]);
+                store_stream(residual_out, off, ro[k]);
             } else {
                 ro[k] = x[0];
             }
@@ -294,16 +287,15 @@ __device__ __forceinline__ void row_pass(const RowArgs &a, float eps, float inv_
     }
 }
 
-template <int N, int PPT, bool kBpermute, bool kResidual, bool kStream,
-          bool kPlainResidualOut = false>
+template <int N, int PPT, bool kBpermute, bool kResidual, bool kStream>
 __global__ void __launch_bounds__(1024) k_rows(RowArgs a)
 {
     __shared__ float slots[kMaxWaves];
     float eps = a.eps, inv_hidden = a.inv_hidden;
     int tiny_eps = a.tiny_eps;
     args_in_sgprs(a, eps, inv_hidden, tiny_eps);
-    row_pass<N, PPT, kBpermute, kResidual, kStream, kPlainResidualOut>(a, eps, inv_hidden,
-                                                                        tiny_eps, blockIdx.x, slots);
+    row_pass<N, PPT, kBpermute, kResidual, kStream>(a, eps, inv_hidden, tiny_eps, blockIdx.x,
+                                                     slots);
 }
 
 // Flat N-way reduce: thread t of workgroup b handles pack b * blockDim.x + t (one pack per thread;
