@@ -3,8 +3,9 @@
 One step = one call of the whole path (N-way fp32 reduce, residual add, RMSNorm) over one batch:
 N = 8 bf16 partial sums of shape [m = 4096, hidden = 7168] (a tensor-parallel degree of 8 at a
 7168-wide hidden state), a bf16 residual and a bf16 weight, synthetic values drawn as N(0, 0.5^2),
-N(0, 1) and 1 + 0.1 N(0, 1). Inputs are resident in HBM when timing starts; two copies of every
-buffer alternate between steps so that the working set (1.3 GB) exceeds the 256 MB Infinity Cache.
+N(0, 1) and 1 + 0.1 N(0, 1). Inputs are resident in HBM when timing starts; six copies of every
+buffer take turns between steps (3.9 GB), so that no read comes from the 256 MB Infinity Cache and
+no output plane is still held there when it is written again (see cold_copies).
 
 Prints one JSON line: the achieved HBM bandwidth on algorithmic bytes, 2 (N + 3) m hidden +
 2 hidden per call, as `value` (GB/s), with the one-stage kernel's roofline, the per-call latency
@@ -149,7 +150,8 @@ def hbm_ceilings(torch):
     """Practical HBM ceilings on this GPU from the plain streaming kernels of hbm_probe/ (libhbm_probe.so): one
     read stream, a copy, and the one-stage kernel's mix of nine read and two write streams at its
     bench shape (N=8, m=4096, hidden=7168), each over a few launch shapes and cache policies,
-    HBM-cold (4 GiB read buffer; 2 GiB copies; two alternating mix sets of 646 MB); then the
+    HBM-cold (4 GiB read buffer; 2 GiB copies; mix sets of 646 MB taking turns, as many as
+    cold_copies asks for); then the
     one-stage kernel itself on that shape in the same process. One JSON line per measurement, then
     a summary line with the best of each and the kernel's rate over the best mix."""
     import hbm_probe
@@ -203,7 +205,7 @@ def hbm_ceilings(torch):
     n, m, hidden = 8, 4096, 7168
     plane = m * hidden * 2
     sets = []
-    for _ in range(2):
+    for _ in range(cold_copies(11 * plane, 2 * plane)):
         t = torch.empty(11 * plane, dtype=torch.uint8, device="cuda")
         t.fill_(1)
         ins = (vp * 9)(*[t.data_ptr() + k * plane for k in range(9)])
@@ -211,14 +213,16 @@ def hbm_ceilings(torch):
         sets.append((t, ins, outs))
     for nt in (3, 1):
         for grid in (8192, 14336):
-            ms = timed_ms(lambda i: check(lib.hbm_probe_mix(sets[i % 2][1], sets[i % 2][2],
-                                                            plane // 16, nt, grid, stream)), 40)
+            ms = timed_ms(lambda i: check(lib.hbm_probe_mix(sets[i % len(sets)][1],
+                                                            sets[i % len(sets)][2],
+                                                            plane // 16, nt, grid, stream)), 48)
             report("mix9r2w", 11 * plane, ms, nt=nt, grid=grid)
     del sets
     torch.cuda.empty_cache()
     # the one-stage kernel on the same traffic, in the same process, for a side-by-side ratio
     import all_reduce_residual_way_amd as fa
-    work = DeviceWorkload(torch, fa, n, m, hidden, 2, seed=1)
+    work = DeviceWorkload(torch, fa, n, m, hidden,
+                          cold_copies(11 * plane, outputs_bytes(m, hidden)), seed=1)
     ms = work.time_ms(1, 200, 20)
     report("onestage", algorithmic_bytes(n, m, hidden), ms, n=n, m=m, hidden=hidden)
     print(json.dumps({"hbm_ceilings_gbs": {k: round(v, 1) for k, v in best.items()},
@@ -229,7 +233,7 @@ def hbm_ceilings(torch):
 
 
 class Workload:
-    """Device buffers of one problem (optionally two copies, alternated between calls) and raw
+    """Device buffers of one problem (optionally several copies, taking turns between calls) and raw
     calls into the library on the current stream."""
 
     def __init__(self, torch, fa, prob, copies):
@@ -447,16 +451,31 @@ def timing_for(work, path, footprint, bytes_alg, options=None):
         return (work.graph_latency_us(path, options, calls=calls, replays=20),
                 f"warm, graph of {calls} calls, min of 20 replays")
     copies = len(work.sets)
-    return (work.time_ms(path, 100, 10, options) * 1e3,
+    return (work.time_ms(path, 100, max(10, copies), options) * 1e3,
             f"100 calls over {copies} buffer sets ({copies * footprint >> 20} MiB)")
 
 
-def cold_copies(footprint):
-    """Buffer sets that make a timed loop read beyond the Infinity Cache (>= 1 GiB in total);
-    one for problems that fit the cache (they are timed warm)."""
+MAX_SETS = 32
+
+
+def cold_copies(footprint, written=None):
+    """Buffer sets for an HBM-cold timed loop over a problem of `footprint` bytes whose calls write
+    `written` bytes each; one for problems that fit the Infinity Cache (they are timed warm). The
+    sets together hold at least 1 GiB, so that reads cannot come from the 256 MB cache, and between
+    two calls on one set the other sets' calls write at least 512 MiB, twice the cache, so that no
+    output plane is still in the cache when it is written again: a rewrite of lines still held
+    there need not reach HBM, which would flatter kernels that store with ordinary stores."""
     if footprint <= (128 << 20):
         return 1
-    return min(8, max(1, -(-(1 << 30) // footprint)))
+    sets = -(-(1 << 30) // footprint)
+    if written:
+        sets = max(sets, 1 + -(-(512 << 20) // written))
+    return max(1, min(MAX_SETS, sets))
+
+
+def outputs_bytes(m, hidden):
+    """Bytes a call writes at least: residual_out and out."""
+    return 4 * m * hidden
 
 
 def all_workloads(torch, fa, synth, oracle):
@@ -471,7 +490,7 @@ def all_workloads(torch, fa, synth, oracle):
             prob = synth.make_problem(n, m, hidden, seed=1000 + m, eps=w["eps"], dist=w["dist"],
                                       name=wname)
             footprint = 2 * (n + 3) * m * hidden
-            work = Workload(torch, fa, prob, cold_copies(footprint))
+            work = Workload(torch, fa, prob, cold_copies(footprint, outputs_bytes(m, hidden)))
             bytes_alg = algorithmic_bytes(n, m, hidden)
             for p in paths:
                 us, how = timing_for(work, p, footprint, bytes_alg)
@@ -503,7 +522,8 @@ def path_sweep(torch, fa, ns=PATH_SWEEP_N, hiddens=PATH_SWEEP_HIDDEN, ms=PATH_SW
                 footprint = 2 * (n + 3) * m * hidden
                 if footprint > (3 << 30):
                     continue
-                work = DeviceWorkload(torch, fa, n, m, hidden, cold_copies(footprint),
+                work = DeviceWorkload(torch, fa, n, m, hidden,
+                                      cold_copies(footprint, outputs_bytes(m, hidden)),
                                       seed=n + hidden + m)
                 bytes_alg = algorithmic_bytes(n, m, hidden)
                 us = {}
@@ -532,7 +552,8 @@ def chunk_sweep(torch, fa):
     on HBM-cold shapes (buffer sets of >= 1 GiB): 60 calls per variant, best of three rounds."""
     for n, m, hidden in CHUNK_SWEEP_SHAPES:
         footprint = 2 * (n + 3) * m * hidden
-        work = DeviceWorkload(torch, fa, n, m, hidden, cold_copies(footprint), seed=m + hidden)
+        work = DeviceWorkload(torch, fa, n, m, hidden, cold_copies(footprint, outputs_bytes(m, hidden)),
+                              seed=m + hidden)
         bytes_alg = algorithmic_bytes(n, m, hidden)
         variants = [("path1", 1, None), ("path2", 2, None),
                     ("path2_pages_split", 2, fa.Options(0, 0, 0, 0, 0, 0, 0, fa.RESIDUAL_STAGE2))]
@@ -639,7 +660,8 @@ def sweep(torch, fa, n=8):
             footprint = 2 * (n + 3) * m * hidden
             if footprint > (2 << 30):
                 continue
-            work = DeviceWorkload(torch, fa, n, m, hidden, cold_copies(footprint), seed=hidden + m)
+            work = DeviceWorkload(torch, fa, n, m, hidden,
+                                  cold_copies(footprint, outputs_bytes(m, hidden)), seed=hidden + m)
             bytes_alg = algorithmic_bytes(n, m, hidden)
             us, how = timing_for(work, 1, footprint, bytes_alg)
             k = fa.describe_launch(n, m, hidden, 1)["kernels"][0]
@@ -703,7 +725,8 @@ def main():
     n, m, hidden, eps, path = args.n, args.m, args.hidden, args.eps, args.path
     log(f"generating n={n} m={m} hidden={hidden}")
     prob = synth.make_problem(n, m, hidden, seed=args.seed, eps=eps, name="bandwidth")
-    work = Workload(torch, fa, prob, copies=2)
+    sets = max(2, cold_copies(2 * (n + 3) * m * hidden, outputs_bytes(m, hidden)))
+    work = Workload(torch, fa, prob, copies=sets)
     bytes_alg = algorithmic_bytes(n, m, hidden)
     plan = fa.describe_launch(n, m, hidden, path)
 
@@ -753,8 +776,8 @@ def main():
             continue
         log(f"metric row m={mm}")
         fp = 2 * (8 + 3) * mm * 7168
-        mw = DeviceWorkload(torch, fa, 8, mm, 7168, min(8, max(1, -(-(1 << 30) // fp))), seed=mm)
-        mus = mw.time_ms(1, max(short, 20), args.warmup) * 1e3
+        mw = DeviceWorkload(torch, fa, 8, mm, 7168, cold_copies(fp, outputs_bytes(mm, 7168)), seed=mm)
+        mus = mw.time_ms(1, max(short, 20), max(args.warmup, len(mw.sets))) * 1e3
         mg = algorithmic_bytes(8, mm, 7168) / (mus * 1e-6) / 1e9
         metric_rows[str(mm)] = {"us_per_call": round(mus, 3), "gbs_algorithmic": round(mg, 1),
                                 "pct_of_hbm_peak": round(100 * mg / HBM_PEAK_GBS, 2),
@@ -860,7 +883,7 @@ def main():
         "config": {"workload": f"fused reduce + residual + RMSNorm, N={n} bf16 partial sums "
                                f"[m={m}, hidden={hidden}], eps={eps}",
                    "n_inputs": n, "m": m, "hidden": hidden, "path": path,
-                   "buffer_sets": 2, "launch": plan["kernels"]},
+                   "buffer_sets": len(work.sets), "launch": plan["kernels"]},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,

@@ -73,7 +73,14 @@ def test_cold_copies_exceed_the_cache():
     assert bench.cold_copies(100 << 20) == 1          # timed warm
     for fp in (200 << 20, 646 << 20, 1 << 30, 3 << 30):
         c = bench.cold_copies(fp)
-        assert c * fp >= (1 << 30) or c == 8
+        assert c * fp >= (1 << 30) or c == bench.MAX_SETS
+    # between two calls on one set the other sets write at least twice the 256 MB cache
+    for n, m, hidden in ((8, 4096, 7168), (8, 2048, 7168), (4, 4096, 7168), (8, 8192, 8192),
+                         (8, 1024, 7168), (8, 16384, 2880)):
+        fp, w = 2 * (n + 3) * m * hidden, bench.outputs_bytes(m, hidden)
+        c = bench.cold_copies(fp, w)
+        assert c * fp >= (1 << 30) and (c - 1) * w >= (512 << 20) and c <= bench.MAX_SETS
+    assert bench.cold_copies(646 << 20, bench.outputs_bytes(4096, 7168)) == 6  # the bench shape
 
 
 def test_load_source_shapes_straddle_the_stream_rule():
