@@ -424,8 +424,8 @@ struct Plan {
 // Where the two-stage path adds the residual. In stage 1 unless the caller asks for the pages'
 // split, or for a form that exists only with it (the LDS-staged stage 1, chunks of rows): then
 // stage 1 stores the reduced rows into `out` and stage 2 reads them back and adds the residual.
-// Measured on MI355X (HBM-cold, bit-identical results): n = 4, m = 4096, hidden 7168 86.5 ->
-// 78.0 us; n = 8, 8192 x 8192 274.5 -> 256.6 us; n = 8, m = 4096, hidden 7168 126.8 -> 117.5 us:
+// Measured on MI355X (HBM-cold, bit-identical results): n = 4, m = 4096, hidden 7168 89.2 ->
+// 80.7 us; n = 8, 8192 x 8192 289.1 -> 272.9 us; n = 8, m = 4096, hidden 7168 131.5 -> 124.0 us:
 // one plane less read and one less written.
 bool residual_in_stage1(const Options &o)
 {

@@ -199,7 +199,7 @@ enum {
  *   residual_out and normalises: 2 (n + 5) m hidden bytes moved.
  * - STAGE1: stage 1 reduces, adds the residual and writes residual_out; stage 2 is a plain
  *   RMSNorm of residual_out: 2 (n + 4) m hidden bytes, no scratch. Bit-identical to STAGE2 (the
- *   same roundings in the same order). On one GPU this is the faster split (by 7-10 % at the
+ *   same roundings in the same order). On one GPU this is the faster split (by 5-10 % at the
  *   bandwidth sizes). Across GPUs the pages keep the reduced rows in a buffer registered for
  *   peer stores, which the caller's residual_out need not be.
  * - AUTO: STAGE1, except with the LDS-staged stage 1 or with chunks of rows, which exist only for
