@@ -149,7 +149,9 @@ def copy_calibration(torch):
 def hbm_ceilings(torch):
     """Practical HBM ceilings on this GPU from the plain streaming kernels of hbm_probe/ (libhbm_probe.so): one
     read stream, a copy, and the one-stage kernel's mix of nine read and two write streams at its
-    bench shape (N=8, m=4096, hidden=7168), each over a few launch shapes and cache policies,
+    bench shape (N=8, m=4096, hidden=7168), each over a few launch shapes and cache policies (then
+    the mixes of the two-stage path's first stage, nine or five reads and one write, and of the
+    one-stage kernel at N=4, five reads and two writes, on planes of the same size),
     HBM-cold (4 GiB read buffer; 2 GiB copies; mix sets of 646 MB taking turns, as many as
     cold_copies asks for); then the
     one-stage kernel itself on that shape in the same process. One JSON line per measurement, then
@@ -219,6 +221,25 @@ def hbm_ceilings(torch):
             report("mix9r2w", 11 * plane, ms, nt=nt, grid=grid)
     del sets
     torch.cuda.empty_cache()
+    # the traffic of the two-stage path's first stage (N + 1 reads, one write; N = 8 and 4) and of
+    # the one-stage kernel at N = 4 (five reads, two writes), on planes of the same size
+    for reads, writes in ((9, 1), (5, 1), (5, 2)):
+        nplanes = reads + writes
+        rsets = []
+        for _ in range(cold_copies(nplanes * plane, writes * plane)):
+            t = torch.empty(nplanes * plane, dtype=torch.uint8, device="cuda")
+            t.fill_(1)
+            ins = (vp * reads)(*[t.data_ptr() + k * plane for k in range(reads)])
+            outs = (vp * writes)(*[t.data_ptr() + (reads + k) * plane for k in range(writes)])
+            rsets.append((t, ins, outs))
+        for nt in (3, 1):
+            def one(i, r=reads, w=writes, nt=nt, sets=rsets):
+                s_ = sets[i % len(sets)]
+                check(lib.hbm_probe_mix_rw(s_[1], r, s_[2], w, plane // 16, nt, 14336, stream))
+            ms = timed_ms(one, 48)
+            report(f"mix{reads}r{writes}w", nplanes * plane, ms, nt=nt, grid=14336)
+        del rsets
+        torch.cuda.empty_cache()
     # the one-stage kernel on the same traffic, in the same process, for a side-by-side ratio
     import all_reduce_residual_way_amd as fa
     work = DeviceWorkload(torch, fa, n, m, hidden,

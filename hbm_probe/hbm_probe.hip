@@ -5,7 +5,9 @@
 //   copy  - one read and one write stream
 //   mix   - nine read streams and two write streams at the same offsets, the byte mix of the
 //           one-stage kernel at N = 8 (eight partial sums and the residual in, residual_out and out
-//           out), with no arithmetic beyond an XOR and an add per pack.
+//           out), with no arithmetic beyond an XOR and an add per pack; mix_rw the same with 5 or 9
+//           read and 1 or 2 write streams (the first stage of the two-stage path at N = 4 and 8
+//           reads N + 1 streams and writes one).
 // Measurement infrastructure for the benchmark only; the fused path does not use it.
 // All kernels are grid-stride loops guarded by the element count. `nt` selects the cache policy:
 // bit 0 non-temporal loads, bit 1 non-temporal stores (3: the fused kernel's policy for HBM-cold
@@ -79,24 +81,27 @@ struct MixArgs {
     size_t packs;  // packs per stream
 };
 
-// out[0] = XOR of the nine inputs, out[1] = out[0] + in[0] (lane-wise 32-bit add).
-template <bool kNTL, bool kNTS>
+// out[0] = XOR of the R inputs, out[1] (when W == 2) = out[0] + in[0] (lane-wise 32-bit add).
+template <int R, int W, bool kNTL, bool kNTS>
 __global__ void __launch_bounds__(kBlock) k_mix(MixArgs a)
 {
+    static_assert(R >= 1 && R <= kMixReads && W >= 1 && W <= kMixWrites, "stream counts");
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.packs; i += stride) {
-        u32x4 v[kMixReads];
+        u32x4 v[R];
 #pragma unroll
-        for (int k = 0; k < kMixReads; ++k)
+        for (int k = 0; k < R; ++k)
             v[k] = load<kNTL>(a.in[k] + i);
         u32x4 x = v[0];
 #pragma unroll
-        for (int k = 1; k < kMixReads; ++k)
+        for (int k = 1; k < R; ++k)
             x ^= v[k];
         store<kNTS>(a.out[0] + i, x);
-        store<kNTS>(a.out[1] + i, x + v[0]);
+        if constexpr (W == 2)
+            store<kNTS>(a.out[1] + i, x + v[0]);
     }
 }
+
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -104,6 +109,40 @@ int launched()
 {
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? 0 : static_cast<int>(e);
+}
+
+template <int R, int W>
+void launch_mix(const MixArgs &a, int nt, int grid, hipStream_t stream)
+{
+    const dim3 g(static_cast<unsigned>(grid)), b(kBlock);
+    switch (nt) {
+    case 0: hipLaunchKernelGGL((k_mix<R, W, false, false>), g, b, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((k_mix<R, W, true, false>), g, b, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((k_mix<R, W, false, true>), g, b, 0, stream, a); break;
+    default: hipLaunchKernelGGL((k_mix<R, W, true, true>), g, b, 0, stream, a); break;
+    }
+}
+
+// The arguments of a mix of `reads` and `writes` streams, checked: -1 for a bad argument.
+int mix_args(const void *const *in, int reads, void *const *out, int writes, size_t packs, int nt,
+             int grid, MixArgs *a)
+{
+    if (in == nullptr || out == nullptr || packs == 0 || grid < 1 || grid > (1 << 20) || nt < 0 ||
+        nt > 3 || reads < 1 || reads > kMixReads || writes < 1 || writes > kMixWrites)
+        return -1;
+    *a = MixArgs{};
+    for (int k = 0; k < reads; ++k) {
+        if (in[k] == nullptr || !aligned16(in[k]))
+            return -1;
+        a->in[k] = static_cast<const u32x4 *>(in[k]);
+    }
+    for (int k = 0; k < writes; ++k) {
+        if (out[k] == nullptr || !aligned16(out[k]))
+            return -1;
+        a->out[k] = static_cast<u32x4 *>(out[k]);
+    }
+    a->packs = packs;
+    return 0;
 }
 
 }  // namespace
@@ -156,27 +195,23 @@ extern "C" int hbm_probe_copy(const void *src, void *dst, size_t packs, int nt, 
 extern "C" int hbm_probe_mix(const void *const *in, void *const *out, size_t packs, int nt,
                              int grid, hipStream_t stream)
 {
-    if (in == nullptr || out == nullptr || packs == 0 || grid < 1 || grid > (1 << 20) || nt < 0 ||
-        nt > 3)
+    MixArgs a;
+    if (mix_args(in, kMixReads, out, kMixWrites, packs, nt, grid, &a) != 0)
         return -1;
-    MixArgs a{};
-    for (int k = 0; k < kMixReads; ++k) {
-        if (in[k] == nullptr || !aligned16(in[k]))
-            return -1;
-        a.in[k] = static_cast<const u32x4 *>(in[k]);
-    }
-    for (int k = 0; k < kMixWrites; ++k) {
-        if (out[k] == nullptr || !aligned16(out[k]))
-            return -1;
-        a.out[k] = static_cast<u32x4 *>(out[k]);
-    }
-    a.packs = packs;
-    const dim3 g(static_cast<unsigned>(grid)), b(kBlock);
-    switch (nt) {
-    case 0: hipLaunchKernelGGL((k_mix<false, false>), g, b, 0, stream, a); break;
-    case 1: hipLaunchKernelGGL((k_mix<true, false>), g, b, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((k_mix<false, true>), g, b, 0, stream, a); break;
-    default: hipLaunchKernelGGL((k_mix<true, true>), g, b, 0, stream, a); break;
-    }
+    launch_mix<kMixReads, kMixWrites>(a, nt, grid, stream);
+    return launched();
+}
+
+// `in`: host array of `reads` device pointers (5 or 9), `out`: host array of `writes` (1 or 2).
+extern "C" int hbm_probe_mix_rw(const void *const *in, int reads, void *const *out, int writes,
+                                size_t packs, int nt, int grid, hipStream_t stream)
+{
+    MixArgs a;
+    if ((reads != 5 && reads != 9) || mix_args(in, reads, out, writes, packs, nt, grid, &a) != 0)
+        return -1;
+    if (reads == 5)
+        writes == 1 ? launch_mix<5, 1>(a, nt, grid, stream) : launch_mix<5, 2>(a, nt, grid, stream);
+    else
+        writes == 1 ? launch_mix<9, 1>(a, nt, grid, stream) : launch_mix<9, 2>(a, nt, grid, stream);
     return launched();
 }

@@ -36,6 +36,13 @@ def test_probe_arguments_rejected_before_launch(probe):
     ins = (VP * 9)(*([FAKE] * 9))
     outs = (VP * 2)(FAKE, FAKE + 4)
     assert probe.hbm_probe_mix(ins, outs, 16, 1, 64, None) == -1
+    outs = (VP * 2)(FAKE, FAKE)
+    assert probe.hbm_probe_mix_rw(ins, 4, outs, 1, 16, 1, 64, None) == -1   # 5 or 9 reads only
+    assert probe.hbm_probe_mix_rw(ins, 9, outs, 3, 16, 1, 64, None) == -1   # 1 or 2 writes
+    assert probe.hbm_probe_mix_rw(ins, 5, outs, 0, 16, 1, 64, None) == -1
+    assert probe.hbm_probe_mix_rw(ins, 9, outs, 1, 0, 1, 64, None) == -1    # no packs
+    ins = (VP * 9)(*([FAKE] * 4 + [None] + [FAKE] * 4))
+    assert probe.hbm_probe_mix_rw(ins, 5, outs, 1, 16, 1, 64, None) == -1   # a null read stream
 
 
 @pytest.mark.gpu
@@ -79,3 +86,21 @@ def test_probes_move_the_bytes_they_claim(probe):
         torch.cuda.synchronize()
         assert torch.equal(outs_t[0], x)
         assert torch.equal(outs_t[1].to(torch.int64).remainder(2**32), want1)
+
+    for reads in (5, 9):
+        xr = ins_t[0].clone()
+        for t in ins_t[1:reads]:
+            xr = torch.bitwise_xor(xr, t)
+        for writes in (1, 2):
+            for nt in (1, 3):
+                outs_t = [torch.zeros_like(src) for _ in range(2)]
+                ins = (VP * reads)(*[t.data_ptr() for t in ins_t[:reads]])
+                outs = (VP * writes)(*[t.data_ptr() for t in outs_t[:writes]])
+                assert probe.hbm_probe_mix_rw(ins, reads, outs, writes, packs, nt, 37, stream) == 0
+                torch.cuda.synchronize()
+                assert torch.equal(outs_t[0], xr)
+                if writes == 2:
+                    want = (xr.to(torch.int64) + ins_t[0].to(torch.int64)).remainder(2**32)
+                    assert torch.equal(outs_t[1].to(torch.int64).remainder(2**32), want)
+                else:
+                    assert not outs_t[1].any()  # the second stream is not written
