@@ -246,10 +246,40 @@ def hbm_ceilings(torch):
                           cold_copies(11 * plane, outputs_bytes(m, hidden)), seed=1)
     ms = work.time_ms(1, 200, 20)
     report("onestage", algorithmic_bytes(n, m, hidden), ms, n=n, m=m, hidden=hidden)
+    del work
+    torch.cuda.empty_cache()
+    # the metric's other rows (m = 2048 and 8192): the nine-read/two-write probe (its best policy
+    # and grid above) and the one-stage kernel on planes of those sizes
+    rows = {}
+    for mm in METRIC_ROWS_M:
+        pl = mm * hidden * 2
+        k = cold_copies(11 * pl, 2 * pl)
+        msets = []
+        for _ in range(k):
+            t = torch.empty(11 * pl, dtype=torch.uint8, device="cuda")
+            t.fill_(1)
+            msets.append((t, (vp * 9)(*[t.data_ptr() + j * pl for j in range(9)]),
+                          (vp * 2)(*[t.data_ptr() + (9 + j) * pl for j in range(2)])))
+        probe_ms = timed_ms(lambda i: check(lib.hbm_probe_mix(msets[i % k][1], msets[i % k][2],
+                                                              pl // 16, 3, 14336, stream)), 48)
+        del msets
+        torch.cuda.empty_cache()
+        mw = DeviceWorkload(torch, fa, n, mm, hidden, cold_copies(11 * pl, outputs_bytes(mm, hidden)),
+                            seed=mm)
+        kernel_ms = mw.time_ms(1, 100, max(20, len(mw.sets)))
+        del mw
+        torch.cuda.empty_cache()
+        probe_gbs = 11 * pl / (probe_ms * 1e-3) / 1e9
+        kernel_gbs = algorithmic_bytes(n, mm, hidden) / (kernel_ms * 1e-3) / 1e9
+        rows[str(mm)] = {"mix9r2w_pct": round(100 * probe_gbs / HBM_PEAK_GBS, 1),
+                         "onestage_pct": round(100 * kernel_gbs / HBM_PEAK_GBS, 1),
+                         "onestage_over_mix9r2w": round(kernel_gbs / probe_gbs, 3), "sets": k}
+        print(json.dumps({"metric_row_m": mm, **rows[str(mm)]}), flush=True)
     print(json.dumps({"hbm_ceilings_gbs": {k: round(v, 1) for k, v in best.items()},
                       "pct_of_hbm_peak": {k: round(100 * v / HBM_PEAK_GBS, 1)
                                           for k, v in best.items()},
-                      "onestage_over_mix9r2w": round(best["onestage"] / best["mix9r2w"], 3)}),
+                      "onestage_over_mix9r2w": round(best["onestage"] / best["mix9r2w"], 3),
+                      "metric_rows": rows}),
           flush=True)
 
 
