@@ -248,8 +248,8 @@ def hbm_ceilings(torch):
     report("onestage", algorithmic_bytes(n, m, hidden), ms, n=n, m=m, hidden=hidden)
     del work
     torch.cuda.empty_cache()
-    # the metric's other rows (m = 2048 and 8192): the nine-read/two-write probe (its best policy
-    # and grid above) and the one-stage kernel on planes of those sizes
+    # the metric's rows (m = 2048, 4096, 8192): the nine-read/two-write probe (non-temporal, one pack
+    # per thread: the best policy and grid above) and the one-stage kernel on planes of those sizes
     rows = {}
     for mm in METRIC_ROWS_M:
         pl = mm * hidden * 2
@@ -260,8 +260,9 @@ def hbm_ceilings(torch):
             t.fill_(1)
             msets.append((t, (vp * 9)(*[t.data_ptr() + j * pl for j in range(9)]),
                           (vp * 2)(*[t.data_ptr() + (9 + j) * pl for j in range(2)])))
+        grid = min(1 << 20, -(-(pl // 16) // 256))  # one pack per thread, as 14336 at m = 4096
         probe_ms = timed_ms(lambda i: check(lib.hbm_probe_mix(msets[i % k][1], msets[i % k][2],
-                                                              pl // 16, 3, 14336, stream)), 48)
+                                                              pl // 16, 3, grid, stream)), 48)
         del msets
         torch.cuda.empty_cache()
         mw = DeviceWorkload(torch, fa, n, mm, hidden, cold_copies(11 * pl, outputs_bytes(mm, hidden)),
