@@ -248,8 +248,8 @@ def hbm_ceilings(torch):
     report("onestage", algorithmic_bytes(n, m, hidden), ms, n=n, m=m, hidden=hidden)
     del work
     torch.cuda.empty_cache()
-    # the metric's rows (m = 2048, 4096, 8192): the nine-read/two-write probe (non-temporal, one pack
-    # per thread: the best policy and grid above) and the one-stage kernel on planes of those sizes
+    # the metric's rows (m = 2048, 4096, 8192): the nine-read/two-write probe (non-temporal, the best
+    # of a few grids) and the one-stage kernel on planes of those sizes
     rows = {}
     for mm in METRIC_ROWS_M:
         pl = mm * hidden * 2
@@ -260,9 +260,12 @@ def hbm_ceilings(torch):
             t.fill_(1)
             msets.append((t, (vp * 9)(*[t.data_ptr() + j * pl for j in range(9)]),
                           (vp * 2)(*[t.data_ptr() + (9 + j) * pl for j in range(2)])))
-        grid = min(1 << 20, -(-(pl // 16) // 256))  # one pack per thread, as 14336 at m = 4096
-        probe_ms = timed_ms(lambda i: check(lib.hbm_probe_mix(msets[i % k][1], msets[i % k][2],
+        probe_ms, probe_grid = float("inf"), 0
+        for grid in (2048, 4096, 8192, 14336, 28672):  # the best of a few grid-stride launch shapes
+            t_ms = timed_ms(lambda i: check(lib.hbm_probe_mix(msets[i % k][1], msets[i % k][2],
                                                               pl // 16, 3, grid, stream)), 48)
+            if t_ms < probe_ms:
+                probe_ms, probe_grid = t_ms, grid
         del msets
         torch.cuda.empty_cache()
         mw = DeviceWorkload(torch, fa, n, mm, hidden, cold_copies(11 * pl, outputs_bytes(mm, hidden)),
@@ -272,7 +275,7 @@ def hbm_ceilings(torch):
         torch.cuda.empty_cache()
         probe_gbs = 11 * pl / (probe_ms * 1e-3) / 1e9
         kernel_gbs = algorithmic_bytes(n, mm, hidden) / (kernel_ms * 1e-3) / 1e9
-        rows[str(mm)] = {"mix9r2w_pct": round(100 * probe_gbs / HBM_PEAK_GBS, 1),
+        rows[str(mm)] = {"mix9r2w_pct": round(100 * probe_gbs / HBM_PEAK_GBS, 1), "grid": probe_grid,
                          "onestage_pct": round(100 * kernel_gbs / HBM_PEAK_GBS, 1),
                          "onestage_over_mix9r2w": round(kernel_gbs / probe_gbs, 3), "sets": k}
         print(json.dumps({"metric_row_m": mm, **rows[str(mm)]}), flush=True)
