@@ -184,6 +184,44 @@ def test_reduce_subnormal_sums():
     assert (want & 0x7FFF).any()
 
 
+def test_non_finite_partial_sums():
+    """Partial sums holding +-inf: the fp32 sums (inf, and inf - inf = NaN), residual_out, and the
+    rows whose square-sum is infinite (out = +-0, NaN where residual_out is infinite) or NaN (the
+    whole row NaN) match the oracle on every path and in the reduce alone, NaN for NaN (a NaN's
+    sign and payload are not compared: the binary32 oracle takes the host's default NaN)."""
+    base = synth.make_problem(4, 6, 1024, seed=71, name="non-finite")
+    ins = [x.copy() for x in base.inputs]
+    ins[1][0, 5] = 0x7F80                            # row 0: +inf in one input
+    ins[0][1, 9], ins[3][1, 9] = 0x7F80, 0xFF80      # row 1: +inf + -inf = NaN
+    ins[2][2, 100], ins[3][2, 100] = 0xFF80, 0xFF80  # row 2: -inf twice
+    p = synth.Problem(ins, base.residual, base.weight, base.eps)
+    want_red = oracle.reduce(ins)
+    want_ro, want_out = oracle.fused(ins, p.residual, p.weight, p.eps)
+    assert is_nan(want_out[1]).all() and is_nan(want_out[0]).sum() == 1  # what the case is for
+
+    def same(got, want, what):
+        gn, wn = is_nan(got), is_nan(want)
+        assert np.array_equal(gn, wn), f"{what}: NaN positions differ"
+        assert np.array_equal(got[~gn], want[~wn]), f"{what}: values differ"
+
+    announce("non-finite partial sums: reduce")
+    red = fa.fused_ar_reduce([dev(x) for x in ins])
+    torch.cuda.synchronize()
+    same(host(red), want_red, "reduce")
+    for path in (1, 2, fa.PATH_UNFUSED):
+        announce(f"non-finite partial sums: path {path}")
+        if path == fa.PATH_UNFUSED:
+            ro_t, out_t = fa.fused_ar_unfused_rmsnorm([dev(x) for x in ins], dev(p.residual),
+                                                      dev(p.weight), p.eps)
+            torch.cuda.synchronize()
+            ro, out = host(ro_t), host(out_t)
+        else:
+            ro, out = run_gpu(p, path)
+        same(ro, want_ro, f"path {path} residual_out")
+        same(out[:3], want_out[:3], f"path {path} out, non-finite rows")
+        assert ulp_diff(out[3:], want_out[3:]).max() <= 1, f"path {path} out, finite rows"
+
+
 # ------------------------------------------------------------------------- hand-worked cases
 
 @pytest.mark.parametrize("fixture", ["reduce_hidden8.txt", "rmsnorm_hidden8.txt"])
