@@ -377,6 +377,20 @@ def test_rejects_aliasing_out_on_gpu_tensors():
     assert e.value.status == fa.ERR_ALIAS
 
 
+@pytest.mark.parametrize("path", [1, 2])
+def test_read_only_buffers_may_alias(path):
+    """Read-only buffers may be the same memory: one tensor passed as three of the four partial
+    sums and as the residual gives the oracle's result for those repeated arrays."""
+    p = synth.make_problem(2, 37, 4096, seed=14, name="aliased inputs")
+    x, y = dev(p.inputs[0]), dev(p.inputs[1])
+    announce(f"aliased read-only buffers path={path}")
+    ro, out = fa.fused_ar_rmsnorm([x, x, y, x], x, dev(p.weight), p.eps, path=path)
+    torch.cuda.synchronize()
+    a, b = p.inputs
+    want_ro, want_out = oracle.fused([a, a, b, a], a, p.weight, p.eps)
+    assert_parity(f"aliased path={path}", host(ro), host(out), want_ro, want_out)
+
+
 # ------------------------------------------------------------------------- invariants
 
 @pytest.mark.parametrize("path", [1, 2])
