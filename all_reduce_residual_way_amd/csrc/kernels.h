@@ -4,19 +4,20 @@
 //                      With N inputs it is the one-stage path (aiter PR #3817, Technical Details >
 //                      1stage); with N = 1 reading the reduced rows it is stage 2 of the two-stage
 //                      path (Technical Details > 2stage > stage-2 RMSNorm reduce).
-//   k_flat_reduce<N>   stage 1 of the two-stage path: one thread per pack, N-way fp32 reduce,
-//                      one bf16 store, no LDS and no workgroup barrier (Technical Details >
-//                      2stage > reduce-scatter).
+//   k_flat_reduce<N>   stage 1 of the two-stage path in the pages' split, and the reduce alone:
+//                      one thread per pack, N-way fp32 reduce, one bf16 store, no LDS and no
+//                      workgroup barrier (Technical Details > 2stage > reduce-scatter).
 //   k_split_reduce<N>, k_split_norm
 //                      split rows: the one-stage result with each row cut into slices on separate
 //                      workgroups, the second kernel combining the slices' square-sums.
-//   k_flat_residual<N> stage 1 with the residual add moved into it (writes residual_out).
+//   k_flat_residual<N> stage 1 with the residual add moved into it (writes residual_out): the
+//                      two-stage path's default first kernel.
 //   k_pipe<N, PPT>     the two-stage path in row chunks: stage 2 of one chunk and stage 1 of the
 //                      next in one launch.
 //   k_stage1_lds<N>    the LDS-staged, one-wave-per-input stage 1 that the flat reduce replaced,
 //                      kept for comparison.
 //
-// Both read and write 16-byte packs of eight bf16; a row of `hidden` elements is hidden / 8 packs
+// All read and write 16-byte packs of eight bf16; a row of `hidden` elements is hidden / 8 packs
 // and consecutive lanes touch consecutive packs, so every wave access is 1 KiB contiguous.
 #pragma once
 
