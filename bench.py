@@ -455,6 +455,53 @@ def design_options(fa):
     }
 
 
+def streaming_probe(torch, n, m, hidden, written):
+    """The practical ceiling of the one-stage kernel's traffic on this GPU: a plain grid-stride
+    streaming kernel (hbm_probe/, non-temporal loads and stores, one XOR per pack) moving n + 1 read
+    and two write streams of [m, hidden] bf16 planes, HBM-cold over buffer sets taking turns as the
+    bench's own, at the best of three launch shapes. GB/s on those bytes, or None when the probe
+    library is not built or n + 1 is not 5 or 9."""
+    if n + 1 not in (5, 9):
+        return None
+    try:
+        import hbm_probe
+        lib = hbm_probe.load()
+    except RuntimeError:
+        return None
+    vp = ctypes.c_void_p
+    plane = 2 * m * hidden
+    reads = n + 1
+    stream = torch.cuda.current_stream().cuda_stream
+    sets = []
+    for _ in range(cold_copies((reads + 2) * plane, written)):
+        t = torch.empty((reads + 2) * plane, dtype=torch.uint8, device="cuda")
+        t.fill_(1)
+        sets.append((t, (vp * reads)(*[t.data_ptr() + k * plane for k in range(reads)]),
+                     (vp * 2)(*[t.data_ptr() + (reads + k) * plane for k in range(2)])))
+    best_ms = float("inf")
+    # the best of a few grid-stride launch shapes, one pack per thread among them
+    for grid in sorted({min(1 << 20, max(1, -(-(plane // 16) // 256))), 8192, 14336}):
+        def call(i, grid=grid):
+            s_ = sets[i % len(sets)]
+            if lib.hbm_probe_mix_rw(s_[1], reads, s_[2], 2, plane // 16, 3, grid, stream) != 0:
+                raise RuntimeError("HBM probe failed")
+
+        for i in range(2 * len(sets)):
+            call(i)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(48):
+            call(i)
+        end.record()
+        torch.cuda.synchronize()
+        best_ms = min(best_ms, start.elapsed_time(end) / 48)
+    ms = best_ms
+    del sets
+    torch.cuda.empty_cache()
+    return (reads + 2) * plane / (ms * 1e-3) / 1e9
+
+
 def per_rank_share(torch, fa, work, steps, warmup):
     """One rank's share of the two-stage path in an N-way tensor-parallel group, on local HBM:
     stage 1 reduces only this rank's 1/N slice of the packs (here the first m/N rows), stage 2
@@ -854,6 +901,15 @@ def main():
             for k, (p, o) in design_options(fa).items()}
         extra["per_rank_share"] = per_rank_share(torch, fa, work, short, args.warmup)
         extra["per_rank_share"]["onestage_us"] = round(ms * 1e3, 3)
+        if path == 1 and 2 * (n + 3) * m * hidden > (128 << 20):
+            log("streaming probe of the same traffic")
+            probe = streaming_probe(torch, n, m, hidden, outputs_bytes(m, hidden))
+            if probe is not None:
+                extra["streaming_probe_same_traffic"] = {
+                    "gbs": round(probe, 1), "pct_of_hbm_peak": round(100 * probe / HBM_PEAK_GBS, 2),
+                    "onestage_over_probe": round(gbs / probe, 3),
+                    "what": f"plain grid-stride kernel, {n + 1} read and 2 write streams of the "
+                            "same planes, non-temporal, best of three grids, same rotation"}
 
     decode = None
     decode_designs = None
