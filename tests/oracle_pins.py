@@ -275,6 +275,47 @@ def pin_zero_rows_pass_residual_through(orc):
     assert not is_nan(out).any()
 
 
+def pin_non_finite_closed_forms(orc):
+    """IEEE 754 fixes what infinities and NaNs become in each step, whatever the finite values
+    around them: in the rank sum inf + finite = inf, +inf + -inf = NaN, and a finite fp32 sum past
+    the largest float overflows to inf; the residual add follows the same rules. In the RMSNorm a
+    row of residual_out that holds an infinity and no NaN has an infinite mean of squares, so
+    1/sqrt(mean + eps) is +0: each finite element becomes a zero whose sign is sign(x) xor
+    sign(w), and the infinite element inf * 0 = NaN. A row that holds a NaN is NaN throughout."""
+    rng = np.random.default_rng(23)
+    m, hidden, n = 6, 64, 3
+    ins = [_random_bf16(rng, (m, hidden), -4, 4) for _ in range(n)]
+    res = _random_bf16(rng, (m, hidden), -4, 4)
+    w = _random_bf16(rng, (hidden,), -2, 2)
+    pinf, ninf, big = 0x7F80, 0xFF80, 0x7F7F            # +inf, -inf, largest finite bf16
+    ins[0][0, 5] = pinf                                  # row 0: one rank infinite
+    ins[0][1, 7], ins[2][1, 7] = pinf, ninf              # row 1: opposite infinities meet
+    res[2, 9] = ninf                                     # row 2: residual infinite
+    ins[1][3, 3], res[3, 3] = pinf, ninf                 # row 3: reduce +inf, residual -inf
+    for x in ins:                                        # row 4: 3 x (2 - 2^-7) 2^127 > FLT_MAX
+        x[4, 0] = big
+    special = {(0, 5), (1, 7), (2, 9), (3, 3), (4, 0)}
+
+    red = orc.reduce(ins)
+    assert red[0, 5] == pinf and is_nan(red[1, 7]) and red[3, 3] == pinf and red[4, 0] == pinf
+    ro, out = orc.fused(ins, res, w, 1e-6)
+    assert ro[0, 5] == pinf and is_nan(ro[1, 7]) and ro[2, 9] == ninf
+    assert is_nan(ro[3, 3]) and ro[4, 0] == pinf
+    for r in range(m):                                   # nothing leaks to other elements
+        for j in range(hidden):
+            if (r, j) not in special:
+                assert (ro[r, j] & 0x7F80) != 0x7F80, (r, j)
+    for r in (1, 3):                                     # NaN rows
+        assert is_nan(out[r]).all(), r
+    for r, jinf in ((0, 5), (2, 9), (4, 0)):             # rows with one infinity
+        assert is_nan(out[r, jinf]), r
+        for j in range(hidden):
+            if j != jinf:
+                want = (int(ro[r, j]) ^ int(w[j])) & 0x8000
+                assert out[r, j] == want, (r, j, hex(out[r, j]), hex(want))
+    assert not is_nan(out[5]).any() and (out[5] & 0x7F80 != 0x7F80).all()  # a finite row stays finite
+
+
 PINS = [
     pin_golden_reduce,
     pin_golden_rmsnorm,
@@ -291,6 +332,7 @@ PINS = [
     pin_power_of_two_scaling,
     pin_input_permutation_when_exact,
     pin_zero_rows_pass_residual_through,
+    pin_non_finite_closed_forms,
 ]
 
 

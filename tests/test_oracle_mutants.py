@@ -73,6 +73,10 @@ MUTANTS = [
     ("weight_dropped", "oracle_bf16_round(x * rstd * w)", "oracle_bf16_round(x * rstd)"),
     ("out_sign_lost", "oracle_bf16_round(x * rstd * w)", "oracle_bf16_round(fabs(x * rstd * w))"),
     ("out_times_std", "oracle_bf16_round(x * rstd * w)", "oracle_bf16_round(x / rstd * w)"),
+    ("round_nan_to_inf", "        return (uint16_t)(sign | 0x7FC0u);",
+     "        return (uint16_t)(sign | 0x7F80u);"),
+    ("square_sum_skips_non_finite", "sumsq = sumsq + x * x;",
+     "if (isfinite(x)) sumsq = sumsq + x * x;"),
     ("row_stride_off_by_one", "size_t row = (size_t)r * (size_t)hidden;",
      "size_t row = (size_t)r * (size_t)(hidden - 1);"),
 ]
