@@ -152,8 +152,10 @@ def hbm_ceilings(torch):
     bench shape (N=8, m=4096, hidden=7168), each over a few launch shapes and cache policies (then
     the mixes of the two-stage path's first stage, nine or five reads and one write, and of the
     one-stage kernel at N=4, five reads and two writes, on planes of the same size),
-    HBM-cold (4 GiB read buffer; 2 GiB copies; mix sets of 646 MB taking turns, as many as
-    cold_copies asks for); then the
+    HBM-cold (4 GiB read and write buffer; 2 GiB copies; mix sets of 646 MB taking turns, as many
+    as cold_copies asks for); one write stream alone; the nine-read/two-write bytes split into a
+    read-only launch and a write-only launch (split9r2w), beside the mix that interleaves them;
+    then the
     one-stage kernel itself on that shape in the same process. One JSON line per measurement, then
     a summary line with the best of each and the kernel's rate over the best mix."""
     import hbm_probe
@@ -196,6 +198,12 @@ def hbm_ceilings(torch):
                                                              sink.data_ptr(), nt, unroll, grid,
                                                              stream)), 20)
             report("read", nbytes, ms, nt=nt, unroll=unroll, grid=grid)
+    for nt in (2, 0):  # one write stream, non-temporal or ordinary stores
+        outs1 = (vp * 1)(buf.data_ptr())
+        for grid in (8192, 32768, 65536):
+            ms = timed_ms(lambda i: check(lib.hbm_probe_writes(outs1, 1, nbytes // 16, nt, grid,
+                                                               stream)), 20)
+            report("write", nbytes, ms, nt=nt, grid=grid)
     half = nbytes // 2
     for nt in (3, 1):  # non-temporal loads, with non-temporal or ordinary stores
         for grid in (8192, 65536):
@@ -219,6 +227,15 @@ def hbm_ceilings(torch):
                                                             sets[i % len(sets)][2],
                                                             plane // 16, nt, grid, stream)), 48)
             report("mix9r2w", 11 * plane, ms, nt=nt, grid=grid)
+    # the same bytes with the reads and the writes in separate launches: the nine read streams
+    # alone, then the two write streams alone, back to back on the same sets
+    for grid in (8192, 14336):
+        def split(i, grid=grid):
+            s_ = sets[i % len(sets)]
+            check(lib.hbm_probe_reads(s_[1], 9, plane // 16, sink.data_ptr(), 1, grid, stream))
+            check(lib.hbm_probe_writes(s_[2], 2, plane // 16, 2, grid, stream))
+        ms = timed_ms(split, 48)
+        report("split9r2w", 11 * plane, ms, nt=3, grid=grid)
     del sets
     torch.cuda.empty_cache()
     # the traffic of the two-stage path's first stage (N + 1 reads, one write; N = 8 and 4) and of
@@ -283,6 +300,7 @@ def hbm_ceilings(torch):
                       "pct_of_hbm_peak": {k: round(100 * v / HBM_PEAK_GBS, 1)
                                           for k, v in best.items()},
                       "onestage_over_mix9r2w": round(best["onestage"] / best["mix9r2w"], 3),
+                      "split9r2w_over_mix9r2w": round(best["split9r2w"] / best["mix9r2w"], 3),
                       "metric_rows": rows}),
           flush=True)
 

@@ -1,6 +1,7 @@
 """The benchmark's HBM ceiling probes (libhbm_probe.so, built from hbm_probe.hip by build.py):
 plain streaming kernels for a read stream, a copy, the one-stage kernel's nine-read /
-two-write mix, and mixes of 5 or 9 reads with 1 or 2 writes. Measurement infrastructure for bench.py --ceilings and its test; the fused path
+two-write mix, mixes of 5 or 9 reads with 1 or 2 writes, and a mix's reads alone and its writes
+alone. Measurement infrastructure for bench.py --ceilings and its test; the fused path
 does not use it."""
 import ctypes
 import os
@@ -21,4 +22,6 @@ def load():
     lib.hbm_probe_copy.argtypes = [vp, vp, sz, ci, ci, vp]
     lib.hbm_probe_mix.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), sz, ci, ci, vp]
     lib.hbm_probe_mix_rw.argtypes = [ctypes.POINTER(vp), ci, ctypes.POINTER(vp), ci, sz, ci, ci, vp]
+    lib.hbm_probe_reads.argtypes = [ctypes.POINTER(vp), ci, sz, vp, ci, ci, vp]
+    lib.hbm_probe_writes.argtypes = [ctypes.POINTER(vp), ci, sz, ci, ci, vp]
     return lib

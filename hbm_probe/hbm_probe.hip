@@ -8,6 +8,9 @@
 //           out), with no arithmetic beyond an XOR and an add per pack; mix_rw the same with 5 or 9
 //           read and 1 or 2 write streams (the first stage of the two-stage path at N = 4 and 8
 //           reads N + 1 streams and writes one).
+//   reads / writes - the read streams of a mix alone (XOR-folded, nothing written) and its write
+//           streams alone (a pattern derived from the pack index): timed back to back, the same
+//           bytes as the mix with the reads and the writes in separate launches.
 // Measurement infrastructure for the benchmark only; the fused path does not use it.
 // All kernels are grid-stride loops guarded by the element count. `nt` selects the cache policy:
 // bit 0 non-temporal loads, bit 1 non-temporal stores (3: the fused kernel's policy for HBM-cold
@@ -102,6 +105,40 @@ __global__ void __launch_bounds__(kBlock) k_mix(MixArgs a)
     }
 }
 
+// The R read streams of a mix alone: each pack XOR-folded into a register, written to `sink` only
+// if the fold hits a fixed pattern (as k_read).
+template <int R, bool kNTL>
+__global__ void __launch_bounds__(kBlock) k_reads(MixArgs a, u32x4 *__restrict__ sink)
+{
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    u32x4 fold = {0u, 0u, 0u, 0u};
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.packs; i += stride) {
+        u32x4 v[R];
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+            v[k] = load<kNTL>(a.in[k] + i);
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+            fold ^= v[k];
+    }
+    if (fold.x == 0x9E3779B9u && fold.y == 0x7F4A7C15u && fold.z == 0x85EBCA6Bu &&
+        fold.w == 0xC2B2AE35u)
+        sink[0] = fold;
+}
+
+// The W write streams of a mix alone: pack i of stream k holds {i, i >> 32, k, ~i}.
+template <int W, bool kNTS>
+__global__ void __launch_bounds__(kBlock) k_writes(MixArgs a)
+{
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.packs; i += stride) {
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+            const u32x4 v = {(uint32_t)i, (uint32_t)(i >> 32), (uint32_t)k, ~(uint32_t)i};
+            store<kNTS>(a.out[k] + i, v);
+        }
+    }
+}
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -124,11 +161,14 @@ void launch_mix(const MixArgs &a, int nt, int grid, hipStream_t stream)
 }
 
 // The arguments of a mix of `reads` and `writes` streams, checked: -1 for a bad argument.
+// Either side may be absent (reads == 0 with in == nullptr, or writes == 0 with out == nullptr) for
+// the read-only and write-only kernels; the mixes need both.
 int mix_args(const void *const *in, int reads, void *const *out, int writes, size_t packs, int nt,
              int grid, MixArgs *a)
 {
-    if (in == nullptr || out == nullptr || packs == 0 || grid < 1 || grid > (1 << 20) || nt < 0 ||
-        nt > 3 || reads < 1 || reads > kMixReads || writes < 1 || writes > kMixWrites)
+    if ((in == nullptr && reads != 0) || (out == nullptr && writes != 0) || packs == 0 || grid < 1 ||
+        grid > (1 << 20) || nt < 0 || nt > 3 || reads < 0 || reads > kMixReads || writes < 0 ||
+        writes > kMixWrites || reads + writes == 0)
         return -1;
     *a = MixArgs{};
     for (int k = 0; k < reads; ++k) {
@@ -196,7 +236,7 @@ extern "C" int hbm_probe_mix(const void *const *in, void *const *out, size_t pac
                              int grid, hipStream_t stream)
 {
     MixArgs a;
-    if (mix_args(in, kMixReads, out, kMixWrites, packs, nt, grid, &a) != 0)
+    if (in == nullptr || out == nullptr || mix_args(in, kMixReads, out, kMixWrites, packs, nt, grid, &a) != 0)
         return -1;
     launch_mix<kMixReads, kMixWrites>(a, nt, grid, stream);
     return launched();
@@ -207,11 +247,49 @@ extern "C" int hbm_probe_mix_rw(const void *const *in, int reads, void *const *o
                                 size_t packs, int nt, int grid, hipStream_t stream)
 {
     MixArgs a;
-    if ((reads != 5 && reads != 9) || mix_args(in, reads, out, writes, packs, nt, grid, &a) != 0)
+    if ((reads != 5 && reads != 9) || writes < 1 || mix_args(in, reads, out, writes, packs, nt, grid, &a) != 0)
         return -1;
     if (reads == 5)
         writes == 1 ? launch_mix<5, 1>(a, nt, grid, stream) : launch_mix<5, 2>(a, nt, grid, stream);
     else
         writes == 1 ? launch_mix<9, 1>(a, nt, grid, stream) : launch_mix<9, 2>(a, nt, grid, stream);
+    return launched();
+}
+
+// The read streams of a mix alone: `in` is a host array of `reads` device pointers (5 or 9), each
+// `packs` packs long; `sink` holds one pack. Only bit 0 of `nt` applies (there are no stores).
+extern "C" int hbm_probe_reads(const void *const *in, int reads, size_t packs, void *sink, int nt,
+                               int grid, hipStream_t stream)
+{
+    MixArgs a;
+    if ((reads != 5 && reads != 9) || sink == nullptr || !aligned16(sink) ||
+        mix_args(in, reads, nullptr, 0, packs, nt, grid, &a) != 0)
+        return -1;
+    u32x4 *k = static_cast<u32x4 *>(sink);
+    const dim3 g(static_cast<unsigned>(grid)), b(kBlock);
+    switch (reads * 2 + (nt & 1)) {
+    case 10: hipLaunchKernelGGL((k_reads<5, false>), g, b, 0, stream, a, k); break;
+    case 11: hipLaunchKernelGGL((k_reads<5, true>), g, b, 0, stream, a, k); break;
+    case 18: hipLaunchKernelGGL((k_reads<9, false>), g, b, 0, stream, a, k); break;
+    default: hipLaunchKernelGGL((k_reads<9, true>), g, b, 0, stream, a, k); break;
+    }
+    return launched();
+}
+
+// The write streams of a mix alone: `out` is a host array of `writes` device pointers (1 or 2),
+// each `packs` packs long. Only bit 1 of `nt` applies (there are no loads).
+extern "C" int hbm_probe_writes(void *const *out, int writes, size_t packs, int nt, int grid,
+                                hipStream_t stream)
+{
+    MixArgs a;
+    if (writes < 1 || mix_args(nullptr, 0, out, writes, packs, nt, grid, &a) != 0)
+        return -1;
+    const dim3 g(static_cast<unsigned>(grid)), b(kBlock);
+    switch (writes * 2 + ((nt >> 1) & 1)) {
+    case 2: hipLaunchKernelGGL((k_writes<1, false>), g, b, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((k_writes<1, true>), g, b, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((k_writes<2, false>), g, b, 0, stream, a); break;
+    default: hipLaunchKernelGGL((k_writes<2, true>), g, b, 0, stream, a); break;
+    }
     return launched();
 }

@@ -1,6 +1,7 @@
 """The HBM ceiling probes of the benchmark (libhbm_probe.so): argument checks on the CPU (no kernel is
-launched), and on the GPU that each probe moves exactly the bytes it claims to (copy, XOR/add mix),
-so the ceilings the benchmark reports are measured on correct streaming kernels."""
+launched), and on the GPU that each probe moves exactly the bytes it claims to (copy, XOR/add mix,
+a mix's reads alone and its writes alone), so the ceilings the benchmark reports are measured on
+correct streaming kernels."""
 import ctypes
 import os
 
@@ -43,6 +44,17 @@ def test_probe_arguments_rejected_before_launch(probe):
     assert probe.hbm_probe_mix_rw(ins, 9, outs, 1, 0, 1, 64, None) == -1    # no packs
     ins = (VP * 9)(*([FAKE] * 4 + [None] + [FAKE] * 4))
     assert probe.hbm_probe_mix_rw(ins, 5, outs, 1, 16, 1, 64, None) == -1   # a null read stream
+    ins = (VP * 9)(*([FAKE] * 9))
+    assert probe.hbm_probe_reads(ins, 4, 16, FAKE, 1, 64, None) == -1       # 5 or 9 reads only
+    assert probe.hbm_probe_reads(ins, 9, 16, None, 1, 64, None) == -1       # no sink
+    assert probe.hbm_probe_reads(ins, 9, 16, FAKE + 4, 1, 64, None) == -1   # misaligned sink
+    assert probe.hbm_probe_reads(ins, 9, 0, FAKE, 1, 64, None) == -1        # no packs
+    assert probe.hbm_probe_reads(None, 9, 16, FAKE, 1, 64, None) == -1
+    assert probe.hbm_probe_writes(outs, 0, 16, 2, 64, None) == -1           # 1 or 2 writes
+    assert probe.hbm_probe_writes(outs, 3, 16, 2, 64, None) == -1
+    assert probe.hbm_probe_writes(None, 2, 16, 2, 64, None) == -1
+    assert probe.hbm_probe_writes(outs, 2, 16, 4, 64, None) == -1           # cache policy 0..3
+    assert probe.hbm_probe_writes((VP * 2)(FAKE, FAKE + 8), 2, 16, 2, 64, None) == -1
 
 
 @pytest.mark.gpu
@@ -104,3 +116,28 @@ def test_probes_move_the_bytes_they_claim(probe):
                     assert torch.equal(outs_t[1].to(torch.int64).remainder(2**32), want)
                 else:
                     assert not outs_t[1].any()  # the second stream is not written
+
+    # a mix's reads alone write nothing; its writes alone write pack i of stream k as
+    # {i, i >> 32, k, ~i}
+    for reads in (5, 9):
+        for nt in (0, 1):
+            ins = (VP * reads)(*[t.data_ptr() for t in ins_t[:reads]])
+            assert probe.hbm_probe_reads(ins, reads, packs, sink.data_ptr(), nt, 37, stream) == 0
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum()) == 0
+    idx = torch.arange(packs, dtype=torch.int64)
+    for writes in (1, 2):
+        for nt in (0, 2):
+            outs_t = [torch.zeros_like(src) for _ in range(2)]
+            outs = (VP * writes)(*[t.data_ptr() for t in outs_t[:writes]])
+            assert probe.hbm_probe_writes(outs, writes, packs, nt, 37, stream) == 0
+            torch.cuda.synchronize()
+            for k in range(2):
+                got = outs_t[k].cpu().view(packs, 4).to(torch.int64).remainder(2**32)
+                if k >= writes:
+                    assert not got.any()  # a stream past `writes` is not touched
+                    continue
+                assert torch.equal(got[:, 0], idx)
+                assert not got[:, 1].any()
+                assert torch.equal(got[:, 2], torch.full_like(idx, k))
+                assert torch.equal(got[:, 3], (~idx).remainder(2**32))
