@@ -855,11 +855,11 @@ int static_scratch(float **ptr)
 
 // The automatic path on one GPU, from a sweep of both paths over n = 2..8, hidden = 2880..32768
 // and m = 1..8192 (MI355X, graphs of calls for cache-sized problems, HBM-cold loops above): the
-// one-stage path is faster everywhere (by 3 % to 2.2x) except where a few rows are each too long
-// for one CU. There the two-stage path's flat stage 1 spreads the reads over every CU: with rows
-// that read (n inputs and the residual) at least 336 KiB it wins up to 16 rows, from 432 KiB up
-// to 40 rows and from 512 KiB up to 48 rows (by up to 25 %; e.g. n = 8, hidden = 32768, m = 1:
-// 5.9 against 7.8 us). The thresholds of the pages (fused_ar_auto_path_tp) weigh the link traffic
+// one-stage path is faster or level everywhere (by up to 2.3x) except where a few rows are each
+// too long for one CU. There the two-stage path's flat stage 1 spreads the reads over every CU:
+// with rows that read (n inputs and the residual) at least 336 KiB it wins up to 16 rows, from
+// 432 KiB up to 40 rows and from 512 KiB up to 48 rows (by up to 24 %; e.g. n = 8,
+// hidden = 32768, m = 1: 5.8 against 7.7 us). The thresholds of the pages (fused_ar_auto_path_tp) weigh the link traffic
 // between GPUs, which one GPU does not have.
 struct TwoStageTier {
     uint64_t row_bytes;  // rows reading at least this many bytes...
