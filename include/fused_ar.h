@@ -124,7 +124,7 @@ int fused_ar_unfused_rmsnorm(const fa_bf16 *const *inputs, int n, const fa_bf16 
  * square-sum is grouped by slice). The pages do not describe this form: it applies the reasoning
  * of aiter PR #3817 (Technical Details > 2stage > stage-1 launch config: more workgroups give small
  * problems more CUs) to the one-stage row. Measured on MI355X (N = 8, calls in a HIP graph): faster
- * than fused_ar_rmsnorm from hidden 16384 at m <= 32 (7.7 -> 4.4 us at hidden 32768, m = 1), slower
+ * than fused_ar_rmsnorm from hidden 16384 at m <= 32 (7.6 -> 4.4-4.5 us at hidden 32768, m = 1), slower
  * at hidden <= 7168 and at m = 128, since its second launch costs about a kernel launch.
  *
  *   splits     slices per row, 1..64 (capped at hidden / 8, so that no slice is empty); 0 = one
