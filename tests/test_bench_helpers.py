@@ -81,6 +81,10 @@ def test_cold_copies_exceed_the_cache():
         c = bench.cold_copies(fp, w)
         assert c * fp >= (1 << 30) and (c - 1) * w >= (512 << 20) and c <= bench.MAX_SETS
     assert bench.cold_copies(646 << 20, bench.outputs_bytes(4096, 7168)) == 6  # the bench shape
+    # the metric's other rows (N=8, hidden 7168): 11 sets at m = 2048, 4 at m = 8192
+    for m, sets in ((2048, 11), (4096, 6), (8192, 4)):
+        fp = 2 * 11 * m * 7168
+        assert bench.cold_copies(fp, bench.outputs_bytes(m, 7168)) == sets, m
 
 
 def test_load_source_shapes_straddle_the_stream_rule():
