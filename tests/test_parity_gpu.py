@@ -147,7 +147,8 @@ def test_auto_path_matches_explicit():
 
 @pytest.mark.parametrize("n,m,hidden", [(1, 3, 8), (2, 5, 24), (3, 7, 520), (4, 64, 7168),
                                         (5, 33, 2880), (6, 1, 32768), (7, 9, 1000),
-                                        (8, 257, 7168), (8, 4096, 7168)])
+                                        (8, 257, 7168), (8, 4096, 7168),
+                                        (3, 2, 65544)])  # rows wider than any row kernel takes
 def test_reduce_bit_exact(n, m, hidden):
     p = synth.make_problem(n, m, hidden, seed=n * 100 + m)
     announce(f"reduce n={n} m={m} hidden={hidden}")
