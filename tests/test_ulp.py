@@ -1,4 +1,4 @@
-"""The ulp helpers every parity verdict goes through (tests/ulp.py), against an independent
+"""The ulp helpers every parity comparison goes through (tests/ulp.py), against an independent
 definition: the distance between two finite bf16 values is how many representable values apart
 they are, counted in the sorted list of all finite bf16 values with +0 and -0 as one value."""
 import numpy as np
@@ -24,7 +24,7 @@ def test_ulp_diff_counts_representable_values_between():
     rng = np.random.default_rng(3)
     a = rng.choice(fin, 200_000)
     b = rng.choice(fin, 200_000)
-    # pairs a few values apart, where the 1-ulp verdicts are taken
+    # pairs a few values apart, where the 1-ulp decisions are taken
     near = rng.choice(fin, 50_000)
     step = rng.integers(-3, 4, near.size)
     idx = np.clip(pos[near] + step, 0, pos[finite].max())
