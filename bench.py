@@ -477,8 +477,10 @@ def streaming_probe(torch, n, m, hidden, written):
     """The practical ceiling of the one-stage kernel's traffic on this GPU: a plain grid-stride
     streaming kernel (hbm_probe/, non-temporal loads and stores, one XOR per pack) moving n + 1 read
     and two write streams of [m, hidden] bf16 planes, HBM-cold over buffer sets taking turns as the
-    bench's own, at the best of three launch shapes. GB/s on those bytes, or None when the probe
-    library is not built or n + 1 is not 5 or 9."""
+    bench's own, at the best of three launch shapes; then the same bytes moved by a launch that only
+    reads the n + 1 streams and a launch that only writes the two, back to back (what the traffic
+    reaches when its reads and writes are not interleaved). (GB/s interleaved, GB/s separated) on
+    those bytes, or None when the probe library is not built or n + 1 is not 5 or 9."""
     if n + 1 not in (5, 9):
         return None
     try:
@@ -496,14 +498,9 @@ def streaming_probe(torch, n, m, hidden, written):
         t.fill_(1)
         sets.append((t, (vp * reads)(*[t.data_ptr() + k * plane for k in range(reads)]),
                      (vp * 2)(*[t.data_ptr() + (reads + k) * plane for k in range(2)])))
-    best_ms = float("inf")
-    # the best of a few grid-stride launch shapes, one pack per thread among them
-    for grid in sorted({min(1 << 20, max(1, -(-(plane // 16) // 256))), 8192, 14336}):
-        def call(i, grid=grid):
-            s_ = sets[i % len(sets)]
-            if lib.hbm_probe_mix_rw(s_[1], reads, s_[2], 2, plane // 16, 3, grid, stream) != 0:
-                raise RuntimeError("HBM probe failed")
+    sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
 
+    def timed(call):
         for i in range(2 * len(sets)):
             call(i)
         torch.cuda.synchronize()
@@ -513,11 +510,28 @@ def streaming_probe(torch, n, m, hidden, written):
             call(i)
         end.record()
         torch.cuda.synchronize()
-        best_ms = min(best_ms, start.elapsed_time(end) / 48)
-    ms = best_ms
+        return start.elapsed_time(end) / 48
+
+    best_ms, best_split_ms = float("inf"), float("inf")
+    # the best of a few grid-stride launch shapes, one pack per thread among them
+    for grid in sorted({min(1 << 20, max(1, -(-(plane // 16) // 256))), 8192, 14336}):
+        def mixed(i, grid=grid):
+            s_ = sets[i % len(sets)]
+            if lib.hbm_probe_mix_rw(s_[1], reads, s_[2], 2, plane // 16, 3, grid, stream) != 0:
+                raise RuntimeError("HBM probe failed")
+
+        def separated(i, grid=grid):
+            s_ = sets[i % len(sets)]
+            if (lib.hbm_probe_reads(s_[1], reads, plane // 16, sink.data_ptr(), 1, grid, stream) != 0
+                    or lib.hbm_probe_writes(s_[2], 2, plane // 16, 2, grid, stream) != 0):
+                raise RuntimeError("HBM probe failed")
+
+        best_ms = min(best_ms, timed(mixed))
+        best_split_ms = min(best_split_ms, timed(separated))
     del sets
     torch.cuda.empty_cache()
-    return (reads + 2) * plane / (ms * 1e-3) / 1e9
+    nbytes = (reads + 2) * plane
+    return nbytes / (best_ms * 1e-3) / 1e9, nbytes / (best_split_ms * 1e-3) / 1e9
 
 
 def per_rank_share(torch, fa, work, steps, warmup):
@@ -921,13 +935,18 @@ def main():
         extra["per_rank_share"]["onestage_us"] = round(ms * 1e3, 3)
         if path == 1 and 2 * (n + 3) * m * hidden > (128 << 20):
             log("streaming probe of the same traffic")
-            probe = streaming_probe(torch, n, m, hidden, outputs_bytes(m, hidden))
-            if probe is not None:
+            probes = streaming_probe(torch, n, m, hidden, outputs_bytes(m, hidden))
+            if probes is not None:
+                probe, separated = probes
                 extra["streaming_probe_same_traffic"] = {
                     "gbs": round(probe, 1), "pct_of_hbm_peak": round(100 * probe / HBM_PEAK_GBS, 2),
                     "onestage_over_probe": round(gbs / probe, 3),
                     "what": f"plain grid-stride kernel, {n + 1} read and 2 write streams of the "
-                            "same planes, non-temporal, best of three grids, same rotation"}
+                            "same planes, non-temporal, best of three grids, same rotation",
+                    "reads_then_writes_gbs": round(separated, 1),
+                    "reads_then_writes_pct_of_hbm_peak": round(100 * separated / HBM_PEAK_GBS, 2),
+                    "reads_then_writes_what": "the same bytes moved by a read-only launch then a "
+                                              "write-only launch, an order a fused row cannot take"}
 
     decode = None
     decode_designs = None
