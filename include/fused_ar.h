@@ -21,8 +21,9 @@
  * - bf16 values are raw 16-bit patterns (fa_bf16). Every [m, hidden] array is row-major and
  *   contiguous, so row r starts hidden elements after row r-1; `weight` has hidden elements.
  * - Pointers named "device" are device (HBM) addresses on the current HIP device; the caller owns
- *   all of them. The library allocates nothing, keeps no state between calls and never
- *   synchronises: it enqueues kernels on `stream` and returns. Buffers must stay valid until the
+ *   all of them. The library allocates nothing, keeps no state between calls (apart from the fixed
+ *   scratch of fused_ar_rmsnorm_split_static, below) and never synchronises: it enqueues kernels
+ *   on `stream` and returns. Buffers must stay valid until the
  *   stream has executed the work. Calls may be captured into a HIP graph (the pointers are copied
  *   into the kernel arguments and are baked into the graph).
  * - `inputs` is a HOST array of n device pointers; it is read during the call only.
@@ -63,7 +64,8 @@ enum {
 enum {
     FUSED_AR_PATH_AUTO = 0,     /* fused_ar_auto_path(n, m, hidden) */
     FUSED_AR_PATH_ONESTAGE = 1, /* one kernel, one row per workgroup */
-    FUSED_AR_PATH_TWOSTAGE = 2, /* flat reduce kernel, then residual + RMSNorm kernel */
+    FUSED_AR_PATH_TWOSTAGE = 2, /* a flat reduce kernel (by default it also adds the residual),
+                                   then an RMSNorm kernel; see FUSED_AR_RESIDUAL_* */
     FUSED_AR_PATH_UNFUSED = 3   /* reduce, residual add and RMSNorm as three kernels (only through
                                    fused_ar_unfused_rmsnorm, fused_ar_rmsnorm_ex and
                                    fused_ar_describe_launch) */
