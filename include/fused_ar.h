@@ -94,7 +94,8 @@ enum {
  *                 as its scratch: stage 1 writes the reduced rows there and stage 2 overwrites
  *                 them with the normalised rows.
  *   path          FUSED_AR_PATH_AUTO, _ONESTAGE or _TWOSTAGE (aiter PR #3817, Technical Details >
- *                 1stage / 2stage); both give bit-identical residual_out.
+ *                 1stage / 2stage); both give bit-identical residual_out and out (the row kernels
+ *                 of a call share one geometry and one reduction tree).
  *   stream        HIP stream the kernels are enqueued on (0 = the null stream).
  * Inputs may overlap one another and the weight may overlap inputs or the residual (all are only
  * read). All device pointers must be 16-byte aligned.
