@@ -467,27 +467,35 @@ def test_graph_replay_matches_eager():
     p = synth.make_problem(8, 16, 7168, seed=15)
     ins = [dev(x) for x in p.inputs]
     res, w = dev(p.residual), dev(p.weight)
-    ro_e, out_e = fa.fused_ar_rmsnorm(ins, res, w, p.eps, path=1)
-    ro2_e, out2_e = fa.fused_ar_rmsnorm(ins, res, w, p.eps, path=2)
+    pages_split = fa.Options()
+    pages_split.residual_stage = fa.RESIDUAL_STAGE2
+    calls = [  # path 1, path 2, the pages' residual split, the unfused sequence
+        lambda ro, out: fa.fused_ar_rmsnorm(ins, res, w, p.eps, residual_out=ro, out=out, path=1),
+        lambda ro, out: fa.fused_ar_rmsnorm(ins, res, w, p.eps, residual_out=ro, out=out, path=2),
+        lambda ro, out: fa.fused_ar_rmsnorm(ins, res, w, p.eps, residual_out=ro, out=out, path=2,
+                                            options=pages_split),
+        lambda ro, out: fa.fused_ar_unfused_rmsnorm(ins, res, w, p.eps, residual_out=ro, out=out),
+    ]
+    eager = [call(torch.empty_like(res), torch.empty_like(res)) for call in calls]
     torch.cuda.synchronize()
-    ro, out = torch.empty_like(res), torch.empty_like(res)
-    ro2, out2 = torch.empty_like(res), torch.empty_like(res)
+    bufs = [(torch.empty_like(res), torch.empty_like(res)) for _ in calls]
+    ro, out = bufs[0]
     announce("graph capture")
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for _ in range(20):
-            fa.fused_ar_rmsnorm(ins, res, w, p.eps, residual_out=ro, out=out, path=1)
-            fa.fused_ar_rmsnorm(ins, res, w, p.eps, residual_out=ro2, out=out2, path=2)
+        for _ in range(10):
+            for call, (r, o) in zip(calls, bufs):
+                call(r, o)
     for replay in range(4):
-        for t in (ro, out, ro2, out2):
-            t.zero_()
+        for r, o in bufs:
+            r.zero_()
+            o.zero_()
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        assert torch.equal(ro.view(torch.int16), ro_e.view(torch.int16)), replay
-        assert torch.equal(out.view(torch.int16), out_e.view(torch.int16)), replay
-        assert torch.equal(ro2.view(torch.int16), ro2_e.view(torch.int16)), replay
-        assert torch.equal(out2.view(torch.int16), out2_e.view(torch.int16)), replay
+        for k, ((r, o), (r_e, o_e)) in enumerate(zip(bufs, eager)):
+            assert torch.equal(r.view(torch.int16), r_e.view(torch.int16)), (replay, k)
+            assert torch.equal(o.view(torch.int16), o_e.view(torch.int16)), (replay, k)
     want_ro, want_out = oracle_rows(p)
     assert_parity("graph", host(ro), host(out), want_ro, want_out)
 
